@@ -1,0 +1,185 @@
+/*
+ * fos.h: C ABI of the four-over-six NVFP4 quantizer for AMD MI355X (gfx950).
+ *
+ * Four-over-six is an adaptive NVFP4 block-scaling recipe: every 16-element
+ * block (1x16 along a row, or a 16x16 tile) is encoded twice, once with the
+ * standard map-to-6 scaling (the block amax lands on E2M1 value 6) and once
+ * with a 1.5x larger block scale (map-to-4, the amax lands on 4), and the
+ * candidate with the lower error is stored as packed E2M1 codes plus an E4M3
+ * block scale under an FP32 global scale (pytorch/ao PR "Add the four-over-six
+ * grouped GEMM and dispatcher wiring", recipe commit). The error metric is MAE
+ * or MSE, computed exactly in FP32 or against FP16-rounded decoded values, and
+ * the E4M3 bound is 448 or 256 (radixark/Megatron-LM PR "Fuse NVFP4 fake-QAT
+ * quantize-dequantize with CuTe DSL", "What does this PR do?", numerical
+ * contract).
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are device pointers on the current HIP device. `stream`
+ *    is a hipStream_t on that device (NULL: the null stream). Calls are
+ *    asynchronous: a zero return means the work is enqueued on `stream`.
+ *  - High-precision tensors are row-major [M, K], contiguous, with K a
+ *    multiple of 16; element type bf16, fp16 or fp32 (FOS_BF16 ...); the base
+ *    pointer is 16-byte aligned.
+ *  - Codes: uint8 [M, K/2], element 2j of a row in the low nibble of byte j
+ *    (E2M1: sign bit 3, magnitude codes 0..7 = {0, 0.5, 1, 1.5, 2, 3, 4, 6}).
+ *  - Scales: uint8 [M, K/16] row-major E4M3 (the "fn" variant, max 448). A
+ *    16x16 tile's scale is written to each of its 16 rows, so one decode
+ *    serves both block shapes.
+ *  - Global scales. From an amax A (per tensor, per row or per group) and the
+ *    E4M3 bound B: S_enc = RN(6B / A), clamped to FLT_MAX, or 1 when A is 0,
+ *    inf, NaN or negative; S_dec = RN(1 / S_enc).
+ *  - The library allocates nothing and keeps no state between calls; the
+ *    caller owns every buffer. Outputs are fully written by every successful
+ *    call (padding rows of the grouped call included).
+ *  - Errors: a nonzero return is an FOS_ERR_* code, nothing is enqueued, and
+ *    fos_last_error() returns a description (thread-local). Conditions that
+ *    only the data can reveal (a 16x16 tile whose per-row amax differs, bad
+ *    group offsets) are OR-ed as FOS_STATUS_* bits into the optional device
+ *    word `d_status` (the caller zeroes it; read it after the stream syncs).
+ *  - NaN inputs follow the rule the kernel page (wolfcomos/ao PR "Add a CuTe
+ *    DSL fast-path kernel for four-over-six quantize", description) states:
+ *    block and global amaxes drop NaN, and a NaN element encodes to +6.
+ *  - Every result is bitwise defined: one binary32 operation per step,
+ *    round-to-nearest-even, E4M3/E2M1 casts RNE with saturation, the error
+ *    terms of a block summed by the pinned shuffle-down tree (strides 8, 4, 2,
+ *    1), the map-to-4 candidate kept only on a strictly lower error.
+ */
+#ifndef FOS_H
+#define FOS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FOS_ABI_VERSION 1
+
+/* element types */
+#define FOS_BF16 0
+#define FOS_FP16 1
+#define FOS_FP32 2
+
+/* fos_config.recipe */
+#define FOS_RECIPE_NVFP4 0  /* standard NVFP4: the map-to-6 candidate only */
+#define FOS_RECIPE_4OVER6 1 /* keep the lower-error of map-to-6 and map-to-4 */
+
+/* fos_config.block */
+#define FOS_BLOCK_1X16 0
+#define FOS_BLOCK_16X16 1
+
+/* fos_config.scale_gran: one amax per tensor or one per row */
+#define FOS_PER_TENSOR 0
+#define FOS_PER_ROW 1
+
+/* fos_config.err_metric (four-over-six only) */
+#define FOS_ERR_MAE 0
+#define FOS_ERR_MSE 1
+
+/* fos_config.err_prec (four-over-six only): error against the FP32 decoded
+ * value, or against that value rounded to binary16 */
+#define FOS_ERR_EXACT 0
+#define FOS_ERR_FP16 1
+
+/* fos_amax granularity */
+#define FOS_AMAX_TENSOR 0
+#define FOS_AMAX_ROW 1
+#define FOS_AMAX_BAND16 2 /* max over each 16-row band, written to its 16 rows */
+
+/* return codes */
+#define FOS_OK 0
+#define FOS_ERR_INVALID_ARG 1 /* null pointer, bad enum value, negative size */
+#define FOS_ERR_DTYPE 2       /* element type not supported by this call */
+#define FOS_ERR_SHAPE 3       /* K % 16, M % 16 for 16x16, size limits */
+#define FOS_ERR_ALIGN 4       /* base pointer not 16-byte aligned */
+#define FOS_ERR_CONFIG 5      /* knob combination not supported by this call */
+#define FOS_ERR_DEVICE 6      /* no HIP device, or not a gfx950 device */
+#define FOS_ERR_LAUNCH 7      /* the kernel launch failed (see fos_last_error) */
+
+/* device status bits */
+#define FOS_STATUS_TILE_NONUNIFORM 1 /* 16x16 with a per-row amax that differs within a 16-row band */
+#define FOS_STATUS_BAD_OFFS 2        /* group offsets not monotone, not multiples of 16, or past M_alloc */
+
+typedef struct fos_config {
+    int32_t recipe;     /* FOS_RECIPE_* */
+    int32_t block;      /* FOS_BLOCK_* */
+    int32_t scale_gran; /* FOS_PER_TENSOR | FOS_PER_ROW */
+    int32_t err_metric; /* FOS_ERR_MAE | FOS_ERR_MSE */
+    int32_t err_prec;   /* FOS_ERR_EXACT | FOS_ERR_FP16 */
+    int32_t e4m3_bound; /* 448 or 256 */
+} fos_config;
+
+/* One tensor of a weight list (fos_qdq_list). */
+typedef struct fos_tensor_desc {
+    const void* x;      /* [M, K] input */
+    void* y;            /* [M, K] output, same element type */
+    const float* amax;  /* device FP32 per-tensor amax, [1] */
+    int64_t M;
+    int64_t K;
+} fos_tensor_desc;
+
+int fos_abi_version(void);
+const char* fos_status_string(int status);
+const char* fos_last_error(void);
+
+/* Global amax: NaN-dropping max |x| with start value +0, per tensor
+ * (out[1]), per row (out[M]) or per 16-row band (out[M], M % 16 == 0).
+ * Max is exact and order-free, so the result does not depend on the launch.
+ * The pages compute this with one FP32 torch reduction per tensor before
+ * the quantizer (Megatron-LM PR, "What does this PR do?", fused data path). */
+int fos_amax(const void* x, int dtype, int64_t M, int64_t K, int gran, float* amax_out, void* stream);
+
+/* Quantize x[M, K] to codes[M, K/2] and scales[M, K/16] under `cfg`
+ * (pytorch/ao PR, recipe commit: four_over_six_quantize with per-tensor or
+ * row-scaled global scales and 1x16 or 16x16 blocks).
+ *   amax:     FP32 [1] (FOS_PER_TENSOR) or [M] (FOS_PER_ROW). With 16x16
+ *             blocks a per-row amax must be equal within each 16-row band
+ *             (the tile-uniform contract of the MoE commit); a band that is
+ *             not is flagged in d_status and quantized with its first row's
+ *             amax.
+ *   sdec_out: nullable; receives S_dec per tensor [1] or per row [M].
+ *   d_status: nullable device int32. */
+int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* amax, const fos_config* cfg,
+                 uint8_t* codes, uint8_t* scales, float* sdec_out, int32_t* d_status, void* stream);
+
+/* Fused fake quantization: y[M, K] = the kept candidate's decoded values,
+ * rounded once to the input type (bf16 or fp16, RNE); no codes or scales are
+ * written (Megatron-LM PR, "What does this PR do?": fused data path, caller-
+ * provided FP32 per-tensor amax, 1x16 blocks). Bitwise equal to
+ * nvfp4_dequantize(fos_quantize(x)). The config must be 1x16 per-tensor. */
+int fos_qdq(const void* x, int dtype, int64_t M, int64_t K, const float* amax, const fos_config* cfg, void* y,
+            void* stream);
+
+/* fos_qdq over a list of n independently stored rank-2 tensors of one
+ * element type, in one launch per 64 tensors (the list API of the Megatron-LM
+ * PR maps any number of discrete weights). `descs` is a HOST array; it is
+ * copied into the launch arguments, so the caller may reuse it on return. */
+int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_config* cfg, void* stream);
+
+/* Standard NVFP4 decode, recipe-agnostic (pytorch/ao PR, recipe commit:
+ * nvfp4_dequantize): y = out_dtype(RN(val(q) * RN(sigma * S_dec))) with sdec
+ * per tensor [1] or per row [M]. */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t M, int64_t K, const float* sdec,
+                     int scale_gran, int out_dtype, void* y, void* stream);
+
+/* Grouped (MoE) activation quantize in one launch (pytorch/ao PR, MoE
+ * commit): x[M_alloc, K] holds G token groups back to back; group g owns
+ * rows [offs[g-1], offs[g]) (offs[-1] = 0, cumulative end offsets, multiples
+ * of 16, empty groups allowed) and its rows quantize with the per-row global
+ * scale from group_amax[g]. Rows at or past offs[G-1] are an over-allocated
+ * tail: they are not read, and their codes and scales are written as zero.
+ * The result equals fos_quantize of each group slice with its own per-tensor
+ * amax. cfg must be 1x16; cfg->scale_gran is ignored.
+ *   offs, group_amax: device int32[G], float[G].
+ *   group_sdec_out:   nullable device float[G].
+ * Offsets that break the contract set FOS_STATUS_BAD_OFFS; the outputs are
+ * then unspecified. */
+int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                         const float* group_amax, const fos_config* cfg, uint8_t* codes, uint8_t* scales,
+                         float* group_sdec_out, int32_t* d_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

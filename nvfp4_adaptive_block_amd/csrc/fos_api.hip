@@ -1,0 +1,299 @@
+// fos_api.hip: the C ABI of include/fos.h: argument validation, template
+// dispatch and launch on the caller's stream. Nothing here allocates memory
+// or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fos.h"
+#include "fos_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Largest element count a launch accepts (2^40: far beyond one GPU's HBM,
+// and small enough that every index fits int64 with room).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+// Grid size: enough workgroups (4 waves each) to cover the work, capped at
+// a few per CU so each wave walks a contiguous range.
+int grid_for(int64_t waves_wanted) {
+  int64_t g = (waves_wanted + 3) / 4;
+  const int64_t cap = 256 * 8;  // 256 CUs x 8 workgroups
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+// The current device must be a gfx950 (cached per device ordinal).
+int check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 ok, 2 bad
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(FOS_ERR_DEVICE, "no current HIP device");
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(mu);
+    if (known[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(FOS_ERR_DEVICE, "hipGetDeviceProperties failed");
+      known[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+      if (known[dev] == 2) return fail(FOS_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    }
+    if (known[dev] == 2) return fail(FOS_ERR_DEVICE, "device %d is not gfx950", dev);
+  }
+  return FOS_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) return fail(FOS_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return FOS_OK;
+}
+
+int check_dtype(int dtype) {
+  if (dtype != FOS_BF16 && dtype != FOS_FP16 && dtype != FOS_FP32) return fail(FOS_ERR_DTYPE, "unknown dtype %d", dtype);
+  return FOS_OK;
+}
+
+int check_cfg(const fos_config* c) {
+  if (!c) return fail(FOS_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->recipe != FOS_RECIPE_NVFP4 && c->recipe != FOS_RECIPE_4OVER6) return fail(FOS_ERR_INVALID_ARG, "bad recipe %d", c->recipe);
+  if (c->block != FOS_BLOCK_1X16 && c->block != FOS_BLOCK_16X16) return fail(FOS_ERR_INVALID_ARG, "bad block %d", c->block);
+  if (c->scale_gran != FOS_PER_TENSOR && c->scale_gran != FOS_PER_ROW)
+    return fail(FOS_ERR_INVALID_ARG, "bad scale_gran %d", c->scale_gran);
+  if (c->err_metric != FOS_ERR_MAE && c->err_metric != FOS_ERR_MSE)
+    return fail(FOS_ERR_INVALID_ARG, "bad err_metric %d", c->err_metric);
+  if (c->err_prec != FOS_ERR_EXACT && c->err_prec != FOS_ERR_FP16) return fail(FOS_ERR_INVALID_ARG, "bad err_prec %d", c->err_prec);
+  if (c->e4m3_bound != 448 && c->e4m3_bound != 256) return fail(FOS_ERR_CONFIG, "e4m3_bound must be 448 or 256, got %d", c->e4m3_bound);
+  return FOS_OK;
+}
+
+int check_shape(int64_t M, int64_t K, int block) {
+  if (M < 0 || K < 0) return fail(FOS_ERR_INVALID_ARG, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+  if (K % 16) return fail(FOS_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (block == FOS_BLOCK_16X16 && M % 16) return fail(FOS_ERR_SHAPE, "16x16 blocks need M %% 16 == 0, M=%lld", (long long)M);
+  if (K > 0 && M > kMaxElems / K) return fail(FOS_ERR_SHAPE, "M*K exceeds 2^40 elements");
+  return FOS_OK;
+}
+
+float six_b(const fos_config* c) { return 6.0f * (float)c->e4m3_bound; }
+
+// the error knobs are ignored by the standard recipe: normalize them so the
+// dispatch picks its one instance
+void mode_of(const fos_config* c, int& metric, int& prec) {
+  metric = c->recipe == FOS_RECIPE_NVFP4 ? FOS_ERR_MSE : c->err_metric;
+  prec = c->recipe == FOS_RECIPE_NVFP4 ? FOS_ERR_EXACT : c->err_prec;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fos_abi_version(void) { return FOS_ABI_VERSION; }
+
+const char* fos_status_string(int status) {
+  switch (status) {
+    case FOS_OK: return "ok";
+    case FOS_ERR_INVALID_ARG: return "invalid argument";
+    case FOS_ERR_DTYPE: return "unsupported element type";
+    case FOS_ERR_SHAPE: return "unsupported shape";
+    case FOS_ERR_ALIGN: return "misaligned pointer";
+    case FOS_ERR_CONFIG: return "unsupported configuration";
+    case FOS_ERR_DEVICE: return "device error";
+    case FOS_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* fos_last_error(void) { return g_last_error.c_str(); }
+
+int fos_amax(const void* x, int dtype, int64_t M, int64_t K, int gran, float* amax_out, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if (gran != FOS_AMAX_TENSOR && gran != FOS_AMAX_ROW && gran != FOS_AMAX_BAND16)
+    return fail(FOS_ERR_INVALID_ARG, "bad amax granularity %d", gran);
+  if ((rc = check_shape(M, K, gran == FOS_AMAX_BAND16 ? FOS_BLOCK_16X16 : FOS_BLOCK_1X16))) return rc;
+  if (!amax_out) return fail(FOS_ERR_INVALID_ARG, "amax_out is NULL");
+  if (!aligned(amax_out, 4)) return fail(FOS_ERR_ALIGN, "amax_out not 4-byte aligned");
+  if (M * K > 0 && !x) return fail(FOS_ERR_INVALID_ARG, "x is NULL");
+  if (x && !aligned(x, 16)) return fail(FOS_ERR_ALIGN, "x not 16-byte aligned");
+  if ((rc = check_device())) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (gran != FOS_AMAX_TENSOR && M == 0) return FOS_OK;
+  if (M * K == 0)  // no elements: every amax is +0
+    return launch_status(fos::launch_zero_u32(amax_out, gran == FOS_AMAX_TENSOR ? 1 : M, s));
+  const int64_t n16 = M * K / 16;
+  int grid = grid_for(gran == FOS_AMAX_TENSOR ? (n16 + 63) / 64 : M);
+  return launch_status(fos::launch_amax(dtype, gran, x, M, K, amax_out, grid, s));
+}
+
+int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* amax, const fos_config* cfg,
+                 uint8_t* codes, uint8_t* scales, float* sdec_out, int32_t* d_status, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if ((rc = check_shape(M, K, cfg->block))) return rc;
+  if (!amax) return fail(FOS_ERR_INVALID_ARG, "amax is NULL");
+  if (M * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned(x, 16)) return fail(FOS_ERR_ALIGN, "x not 16-byte aligned");
+  if (!aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "codes not 8-byte aligned");
+  if (!aligned(amax, 4) || !aligned(sdec_out, 4) || !aligned(d_status, 4)) return fail(FOS_ERR_ALIGN, "amax/sdec/status misaligned");
+  if ((rc = check_device())) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int metric, prec;
+  mode_of(cfg, metric, prec);
+  const bool per_row = cfg->scale_gran == FOS_PER_ROW;
+  if (sdec_out && (per_row ? M : 1) > 0)
+    if ((rc = launch_status(fos::launch_sdec(amax, per_row ? M : 1, six_b(cfg), sdec_out, s)))) return rc;
+  if (M * K == 0) return FOS_OK;
+  if (cfg->block == FOS_BLOCK_1X16) {
+    fos::Args1x16<1> a;
+    memset(&a, 0, sizeof a);
+    a.t[0] = fos::TensorRef{x, nullptr, amax, M, K, 0};
+    a.n = 1;
+    a.total_units = (M * (K / 16) + 63) / 64;
+    a.six_b = six_b(cfg);
+    a.codes = codes;
+    a.scales = scales;
+    return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec,
+                                                per_row ? fos::kGranRow : fos::kGranTensor, a,
+                                                grid_for(a.total_units), s));
+  }
+  fos::Args16x16 a;
+  a.x = x;
+  a.y = nullptr;
+  a.amax = amax;
+  a.M = M;
+  a.K = K;
+  a.six_b = six_b(cfg);
+  a.codes = codes;
+  a.scales = scales;
+  a.status = d_status;
+  const int64_t units = (M / 16) * ((K / 16 + 3) / 4);
+  return launch_status(fos::launch_quant_16x16(dtype, cfg->recipe, metric, prec,
+                                               per_row ? fos::kGranRow : fos::kGranTensor, a, grid_for(units), s));
+}
+
+static int check_qdq_cfg(const fos_config* cfg, int dtype) {
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (dtype != FOS_BF16 && dtype != FOS_FP16) return fail(FOS_ERR_DTYPE, "fused QDQ takes bf16 or fp16, got dtype %d", dtype);
+  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
+    return fail(FOS_ERR_CONFIG, "fused QDQ supports 1x16 blocks with a per-tensor amax");
+  return FOS_OK;
+}
+
+int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_config* cfg, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_qdq_cfg(cfg, dtype))) return rc;
+  if (n < 0) return fail(FOS_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !descs) return fail(FOS_ERR_INVALID_ARG, "descs is NULL");
+  for (int i = 0; i < n; i++) {
+    const fos_tensor_desc& d = descs[i];
+    if ((rc = check_shape(d.M, d.K, FOS_BLOCK_1X16))) return fail(rc, "tensor %d: %s", i, g_last_error.c_str());
+    if (!d.amax) return fail(FOS_ERR_INVALID_ARG, "tensor %d: amax is NULL", i);
+    if (d.M * d.K > 0 && (!d.x || !d.y)) return fail(FOS_ERR_INVALID_ARG, "tensor %d: x/y is NULL", i);
+    if (!aligned(d.x, 16) || !aligned(d.y, 16)) return fail(FOS_ERR_ALIGN, "tensor %d: x/y not 16-byte aligned", i);
+    if (!aligned(d.amax, 4)) return fail(FOS_ERR_ALIGN, "tensor %d: amax misaligned", i);
+  }
+  if ((rc = check_device())) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int metric, prec;
+  mode_of(cfg, metric, prec);
+  int i = 0;
+  while (i < n) {
+    fos::Args1x16<fos::kMaxList> a;
+    memset(&a, 0, sizeof a);
+    int64_t units = 0;
+    for (; i < n && a.n < fos::kMaxList; i++) {
+      const fos_tensor_desc& d = descs[i];
+      if (d.M * d.K == 0) continue;
+      a.t[a.n++] = fos::TensorRef{d.x, d.y, d.amax, d.M, d.K, units};
+      units += (d.M * (d.K / 16) + 63) / 64;
+    }
+    if (a.n == 0) continue;
+    a.total_units = units;
+    a.six_b = six_b(cfg);
+    if ((rc = launch_status(fos::launch_qdq_1x16(dtype, cfg->recipe, metric, prec, a, grid_for(units), s)))) return rc;
+  }
+  return FOS_OK;
+}
+
+int fos_qdq(const void* x, int dtype, int64_t M, int64_t K, const float* amax, const fos_config* cfg, void* y,
+            void* stream) {
+  fos_tensor_desc d{x, y, amax, M, K};
+  return fos_qdq_list(1, &d, dtype, cfg, stream);
+}
+
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t M, int64_t K, const float* sdec,
+                     int scale_gran, int out_dtype, void* y, void* stream) {
+  int rc;
+  if ((rc = check_dtype(out_dtype))) return rc;
+  if (scale_gran != FOS_PER_TENSOR && scale_gran != FOS_PER_ROW) return fail(FOS_ERR_INVALID_ARG, "bad scale_gran %d", scale_gran);
+  if ((rc = check_shape(M, K, FOS_BLOCK_1X16))) return rc;
+  if (M * K > 0 && (!codes || !scales || !sdec || !y)) return fail(FOS_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(codes, 8) || !aligned(y, 16) || !aligned(sdec, 4)) return fail(FOS_ERR_ALIGN, "misaligned pointer");
+  if ((rc = check_device())) return rc;
+  if (M * K == 0) return FOS_OK;
+  const int64_t nblk = M * (K / 16);
+  return launch_status(fos::launch_dequant(out_dtype, scale_gran == FOS_PER_ROW ? fos::kGranRow : fos::kGranTensor,
+                                           codes, scales, sdec, M, K, y, grid_for((nblk + 63) / 64),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                         const float* group_amax, const fos_config* cfg, uint8_t* codes, uint8_t* scales,
+                         float* group_sdec_out, int32_t* d_status, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (cfg->block != FOS_BLOCK_1X16) return fail(FOS_ERR_CONFIG, "grouped quantize supports 1x16 blocks");
+  if ((rc = check_shape(M_alloc, K, FOS_BLOCK_1X16))) return rc;
+  if (G <= 0) return fail(FOS_ERR_INVALID_ARG, "G must be positive, got %d", G);
+  if (!offs || !group_amax) return fail(FOS_ERR_INVALID_ARG, "offs and group_amax must be non-NULL");
+  if (M_alloc * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned(x, 16) || !aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "x or codes misaligned");
+  if (!aligned(offs, 4) || !aligned(group_amax, 4) || !aligned(group_sdec_out, 4) || !aligned(d_status, 4))
+    return fail(FOS_ERR_ALIGN, "offs/amax/sdec/status misaligned");
+  if ((rc = check_device())) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int metric, prec;
+  mode_of(cfg, metric, prec);
+  if (d_status)
+    if ((rc = launch_status(fos::launch_check_offs(offs, G, M_alloc, d_status, s)))) return rc;
+  if (group_sdec_out)
+    if ((rc = launch_status(fos::launch_sdec(group_amax, G, six_b(cfg), group_sdec_out, s)))) return rc;
+  if (M_alloc * K == 0) return FOS_OK;
+  fos::Args1x16<1> a;
+  memset(&a, 0, sizeof a);
+  a.t[0] = fos::TensorRef{x, nullptr, nullptr, M_alloc, K, 0};
+  a.n = 1;
+  a.G = G;
+  a.total_units = (M_alloc * (K / 16) + 63) / 64;
+  a.six_b = six_b(cfg);
+  a.codes = codes;
+  a.scales = scales;
+  a.offs = offs;
+  a.group_amax = group_amax;
+  return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, fos::kGranGroup, a,
+                                              grid_for(a.total_units), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// fos_device.h: device-side building blocks of the four-over-six NVFP4
+// quantizer for gfx950 (MI355X).
+//
+// Every function here computes one step of the quantizer bit-exactly: one
+// binary32 operation per step, round to nearest even. Conversions use
+// gfx950's convert instructions where those were checked exhaustively against
+// the format definitions (every binary32 input), and plain integer/float code
+// elsewhere:
+//   - f32 -> E2M1 pair (v_cvt_scalef32_pk_fp4_f32, scale 1.0): RNE with
+//     saturation to +-6 for every non-NaN input, -0 kept; a NaN becomes
+//     (sign | 6), so blocks holding a NaN take the careful path, which encodes
+//     NaN as +6 (the NaN rule the kernel page, wolfcomos/ao PR "Add a CuTe DSL
+//     fast-path kernel for four-over-six quantize", states).
+//   - E2M1 pair -> f32 (v_cvt_scalef32_pk_f32_fp4, scale 1.0): exact.
+//   - f32 -> E4M3 (v_cvt_pk_fp8_f32) on inputs clamped to [0, 448]: RNE.
+//   - E4M3 -> f32 (v_cvt_f32_fp8): exact.
+//   - f32 -> f16 and f32 -> bf16 (v_cvt_f16_f32, v_cvt_pk_bf16_f32): RNE,
+//     overflow to inf, gradual underflow.
+// The build uses -ffp-contract=off and HIP's correctly rounded f32 division.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fos {
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Hide a value from the optimizer so that a following conversion is not
+// fused with the operation that produced it (a fused multiply-and-round to
+// f16 would round once instead of twice).
+__device__ __forceinline__ float opaque(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// ---------------------------------------------------------------- inputs
+
+// bf16 pair in one dword -> two exact binary32 values
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// f16 pair -> two exact binary32 values
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  return (float)h;
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  return (float)h;
+}
+
+// binary32 -> binary16 -> binary32 (RNE, overflow to inf)
+__device__ __forceinline__ float round_f16(float v) {
+  _Float16 h = (_Float16)opaque(v);
+  return (float)h;
+}
+
+// two binary32 -> packed bf16 pair / f16 pair (RNE)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  __bf16 a = (__bf16)opaque(lo), b = (__bf16)opaque(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  _Float16 a = (_Float16)opaque(lo), b = (_Float16)opaque(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ---------------------------------------------------------------- scales
+
+// Global encode scale: S_enc = RN(6B / A) clamped to FLT_MAX, or 1 when A is
+// 0, inf, NaN or negative. six_b = 6 * bound (2688 or 1536, exact).
+__device__ __forceinline__ float global_encode_scale(float A, float six_b) {
+  bool ok = (A > 0.0f) && (A < __builtin_huge_valf());
+  float s = six_b / (ok ? A : 1.0f);
+  s = __builtin_fminf(s, kFltMax);
+  return ok ? s : 1.0f;
+}
+
+// E4M3 code (RNE, saturating at 448) of t >= 0, t not NaN.
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  float tc = __builtin_fminf(t, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tc, tc, 0, false) & 0xFFu;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+// ---------------------------------------------------------------- E2M1
+
+// Eight E2M1 codes (two per byte lane, element 2j in the low nibble) of
+// v[0..7] into one dword. NaN inputs give (sign | 7); see the header note.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
+// Decode eight E2M1 codes of a dword into their values.
+__device__ __forceinline__ void e2m1_unpack8(uint32_t w, float* out) {
+  f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = a.x; out[1] = a.y; out[2] = b.x; out[3] = b.y;
+  out[4] = c.x; out[5] = c.y; out[6] = d.x; out[7] = d.y;
+}
+
+// ---------------------------------------------------------------- reductions
+
+// The pinned width-16 order: strides 8, 4, 2, 1 where position i adds
+// position i + stride (the clamped shuffle-down tree of the kernel page).
+// Overwrites u.
+__device__ __forceinline__ float tree16(float* u) {
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) {
+#pragma unroll
+    for (int i = 0; i < s; i++) u[i] = u[i] + u[i + s];
+  }
+  return u[0];
+}
+
+// The same tree across the 16 lanes of a DPP row (lanes 16k .. 16k+15 hold
+// terms 0..15): after it, lane 16k holds the sum; other lanes hold partials.
+__device__ __forceinline__ float tree16_lanes(float v) {
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 16);
+  return v;
+}
+
+__device__ __forceinline__ float max16_lanes(float v) {
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, s, 16));
+  return v;
+}
+
+}  // namespace fos

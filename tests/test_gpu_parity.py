@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path against the CPU oracle, bit for bit.
+
+Every case feeds the same seeded input bits to both sides; amaxes and group
+offsets come from the oracle or the input generators, never from the GPU.
+Codes, scales and S_dec must match exactly; dequantized and QDQ outputs are
+compared as raw 16-bit patterns (signed zeros included).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_adaptive_block_amd as fos
+import synthdata
+from synthdata import raw_bits
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("nvfp4", "mse", "exact")] + [("4over6", m, p) for m in ("mae", "mse") for p in ("exact", "fp16")]
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return raw_bits(t.cpu())
+
+
+def gpu_quant(x, amax, **kw):
+    codes, scales, sdec = fos.fos_quantize(dev(x), dev(torch.from_numpy(amax)), **kw)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), sdec.cpu().numpy()
+
+
+def assert_quant_equal(orc, x, dtype, amax, label="", **kw):
+    want = orc.quantize(raw_bits(x), dtype, amax, **kw)
+    codes, scales, sdec = gpu_quant(x, amax, **kw)
+    np.testing.assert_array_equal(scales, want["scales"], err_msg=f"scales {label} {kw}")
+    np.testing.assert_array_equal(codes, want["codes"], err_msg=f"codes {label} {kw}")
+    np.testing.assert_array_equal(sdec.view(np.uint32), want["sdec"].view(np.uint32), err_msg=f"sdec {label} {kw}")
+
+
+def _family(family, dtype, M, K, seed):
+    if family == "weight":
+        return synthdata.weight(M, K, seed, dtype)
+    return synthdata.activation_family(family, M, K, seed, dtype)
+
+
+# ------------------------------------------------------------------ 1x16
+
+def test_single_tensor_256x1024(orc):
+    """bf16 256x1024 N(0,1), per-tensor amax, 1x16, bound 448, MSE exact; then every mode."""
+    x = synthdata.normal(256, 1024, 11, "bf16")
+    amax = orc.amax(raw_bits(x), "bf16", "tensor")
+    assert_quant_equal(orc, x, "bf16", amax, recipe="4over6", err_metric="mse", err_prec="exact", bound=448)
+    for (recipe, metric, prec), bound, gran in itertools.product(MODES, (448, 256), ("tensor", "row")):
+        a = amax if gran == "tensor" else orc.amax(raw_bits(x), "bf16", "row")
+        assert_quant_equal(orc, x, "bf16", a, recipe=recipe, err_metric=metric, err_prec=prec, bound=bound,
+                           scale_gran=gran)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("family", synthdata.ACTIVATION_FAMILIES)
+def test_activation_families_all_knobs(orc, dtype, family):
+    """The dense-activation families at a size with ragged rows (K/16 = 97
+    blocks per row, units straddle rows), both global-scale granularities,
+    every mode and both bounds."""
+    M, K = 67, 1552
+    x = _family(family, dtype, M, K, 21 + synthdata.ACTIVATION_FAMILIES.index(family))
+    b = raw_bits(x)
+    am = {"tensor": orc.amax(b, dtype, "tensor"), "row": orc.amax(b, dtype, "row")}
+    for (recipe, metric, prec), bound, gran in itertools.product(MODES, (448, 256), ("tensor", "row")):
+        assert_quant_equal(orc, x, dtype, am[gran], label=family, recipe=recipe, err_metric=metric, err_prec=prec,
+                           bound=bound, scale_gran=gran)
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (1, 1024), (3, 48), (5, 1008), (130, 64), (2, 2064)])
+def test_small_and_ragged_shapes(orc, shape):
+    M, K = shape
+    x = synthdata.activation_family("outlier", M, K, 5, "bf16")
+    b = raw_bits(x)
+    for gran in ("tensor", "row"):
+        a = orc.amax(b, "bf16", gran)
+        for recipe, metric, prec in MODES:
+            assert_quant_equal(orc, x, "bf16", a, recipe=recipe, err_metric=metric, err_prec=prec, scale_gran=gran)
+
+
+def test_caller_amax_edge_values(orc):
+    """Caller amax below the data (scales saturate), zero, inf, NaN, tiny
+    (S_enc clamps to FLT_MAX) and huge."""
+    x = synthdata.activation_family("normal", 32, 256, 6, "fp32")
+    b = raw_bits(x)
+    true = float(orc.amax(b, "fp32", "tensor")[0])
+    for A in (true / 7, 0.0, float("inf"), float("nan"), 1e-38, 1e-45, 3e38, -1.0):
+        a = np.array([A], np.float32)
+        for recipe, metric, prec in MODES:
+            assert_quant_equal(orc, x, "fp32", a, label=f"A={A}", recipe=recipe, err_metric=metric, err_prec=prec)
+
+
+def test_nan_inf_and_signed_zero_blocks(orc):
+    """NaN (quiet and signalling, both signs), +-inf, +-0, subnormals: the
+    careful path and the NaN rule (+6)."""
+    M, K = 16, 64
+    x = np.random.default_rng(3).standard_normal((M, K)).astype(np.float32)
+    u = x.view(np.uint32)
+    u[0, 0] = 0x7FC00000   # qNaN
+    u[1, 5] = 0xFFC00001   # -qNaN
+    u[2, 7] = 0x7F800001   # sNaN
+    u[3, 3] = 0xFF800005   # -sNaN
+    u[3, 4] = 0x7F800001
+    x[4, :16] = np.inf
+    x[5, 3] = -np.inf
+    x[6, :16] = -0.0
+    x[7, :16] = 0.0
+    x[7, 5] = -0.0
+    x[8, :] = 1e-42
+    u[9, :16] = 0x7FC00000  # an all-NaN block: amax +0
+    u[10, 16:32] = 0xFF800001
+    x[10, 20] = 2.5
+    xt = torch.from_numpy(x)
+    for dtype in ("fp32", "bf16", "fp16"):
+        t = xt.to(synthdata.TORCH_DTYPES[dtype])
+        b = raw_bits(t)
+        for gran in ("tensor", "row"):
+            a = orc.amax(b, dtype, gran)
+            for recipe, metric, prec in MODES:
+                assert_quant_equal(orc, t, dtype, a, label=dtype, recipe=recipe, err_metric=metric, err_prec=prec,
+                                   scale_gran=gran)
+
+
+# ------------------------------------------------------------------ 16x16
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_16x16_all_knobs(orc, dtype):
+    """16x16 tiles on weights, 17 tiles per band (the last group of four
+    tiles is ragged), per-tensor and tile-uniform per-row amax."""
+    M, K = 48, 272
+    x = synthdata.weight(M, K, 31, dtype)
+    b = raw_bits(x)
+    am = {"tensor": orc.amax(b, dtype, "tensor"), "row": orc.amax(b, dtype, "band16")}
+    for (recipe, metric, prec), bound, gran in itertools.product(MODES, (448, 256), ("tensor", "row")):
+        assert_quant_equal(orc, x, dtype, am[gran], recipe=recipe, err_metric=metric, err_prec=prec, bound=bound,
+                           scale_gran=gran, block="16x16")
+
+
+def test_16x16_special_data_and_nonuniform_flag(orc):
+    M, K = 32, 128
+    x = synthdata.activation_family("special", M, K, 8, "bf16").to(torch.float32)
+    x[20, 3] = float("nan")
+    x[17, 40] = float("inf")
+    x = x.to(torch.bfloat16)
+    b = raw_bits(x)
+    row = orc.amax(b, "bf16", "row")   # not uniform within bands
+    for recipe, metric, prec in MODES:
+        want = orc.quantize(b, "bf16", row, recipe=recipe, err_metric=metric, err_prec=prec, block="16x16",
+                            scale_gran="row")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        codes, scales, sdec = fos.fos_quantize(dev(x), dev(torch.from_numpy(row)), recipe=recipe, err_metric=metric,
+                                               err_prec=prec, block="16x16", scale_gran="row", status=status)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+        assert want["status"] & fos.STATUS_TILE_NONUNIFORM
+        assert int(status.item()) & fos.STATUS_TILE_NONUNIFORM
+
+
+# ------------------------------------------------------------------ QDQ and dequantize
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_qdq_list_all_modes(orc, dtype):
+    """A list of expert-like weights of different shapes in one call; each
+    output bit-equal to the oracle's fused QDQ."""
+    shapes = [(48, 112), (16, 1024), (33, 2064), (1, 16)]
+    ws = []
+    for i, (M, K) in enumerate(shapes):
+        w = torch.randn(M, K, generator=torch.Generator().manual_seed(100 + i)) * 0.02
+        w.view(-1)[:: 97] *= 50
+        ws.append(w.to(synthdata.TORCH_DTYPES[dtype]))
+    amaxes = [orc.amax(raw_bits(w), dtype, "tensor") for w in ws]
+    for (recipe, metric, prec), bound in itertools.product(MODES, (448, 256)):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+        ys = fos.fos_qdq_list([dev(w) for w in ws], [dev(torch.from_numpy(a)) for a in amaxes], **kw)
+        torch.cuda.synchronize()
+        for w, a, y in zip(ws, amaxes, ys):
+            want = orc.qdq(raw_bits(w), dtype, a, **kw)
+            np.testing.assert_array_equal(bits_of(y), want, err_msg=f"{kw} {tuple(w.shape)}")
+
+
+def test_qdq_single_and_many_tensors(orc):
+    """fos_qdq, and a list longer than one launch holds (two launches)."""
+    ws = [synthdata.weight(16, 64 + 16 * (i % 5), 200 + i, "bf16") for i in range(53)]
+    amaxes = [orc.amax(raw_bits(w), "bf16", "tensor") for w in ws]
+    ys = fos.fos_qdq_list([dev(w) for w in ws], [dev(torch.from_numpy(a)) for a in amaxes], recipe="4over6")
+    y0 = fos.fos_qdq(dev(ws[0]), dev(torch.from_numpy(amaxes[0])), recipe="4over6")
+    torch.cuda.synchronize()
+    for w, a, y in zip(ws, amaxes, ys):
+        np.testing.assert_array_equal(bits_of(y), orc.qdq(raw_bits(w), "bf16", a, recipe="4over6"))
+    np.testing.assert_array_equal(bits_of(y0), bits_of(ys[0]))
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("gran", ["tensor", "row"])
+def test_dequantize(orc, out_dtype, gran):
+    x = synthdata.activation_family("outlier", 40, 320, 14, "bf16")
+    b = raw_bits(x)
+    a = orc.amax(b, "bf16", gran)
+    q = orc.quantize(b, "bf16", a, recipe="4over6", scale_gran=gran)
+    want = orc.dequantize(q["codes"], q["scales"], q["sdec"], gran, out_dtype)
+    y = fos.nvfp4_dequantize(dev(torch.from_numpy(q["codes"])), dev(torch.from_numpy(q["scales"])),
+                             dev(torch.from_numpy(q["sdec"])), gran, synthdata.TORCH_DTYPES[out_dtype])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits_of(y), want)
+
+
+# ------------------------------------------------------------------ grouped
+
+@pytest.mark.parametrize("bound", [448, 256])
+def test_grouped_small(orc, bound):
+    M, pad, K, G = 1024, 64, 272, 16
+    x, offs, fac = synthdata.grouped_tokens(M, pad, K, G, seeds=(61, 62, 63, 64))
+    b = raw_bits(x)
+    starts = np.concatenate([[0], offs[:-1]])
+    gam = np.array([orc.amax(b[s:e], "bf16", "tensor")[0] if e > s else 0.0 for s, e in zip(starts, offs)],
+                   np.float32)
+    want = orc.quantize_grouped(b, "bf16", offs, gam, recipe="4over6", bound=bound)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    codes, scales, gsdec = fos.fos_quantize_grouped(dev(x), dev(torch.from_numpy(offs)), dev(torch.from_numpy(gam)),
+                                                    recipe="4over6", bound=bound, status=status)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+    np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+    np.testing.assert_array_equal(gsdec.cpu().numpy().view(np.uint32), want["group_sdec"].view(np.uint32))
+    assert int(status.item()) == 0
+
+
+def test_grouped_empty_groups_and_bad_offsets(orc):
+    K = 64
+    x = synthdata.normal(96, K, 3, "bf16")
+    offs = np.array([0, 32, 32, 64, 64], np.int32)
+    gam = np.array([5.0, 2.0, 7.0, 3.0, 9.0], np.float32)
+    want = orc.quantize_grouped(raw_bits(x), "bf16", offs, gam, recipe="4over6")
+    codes, scales, _ = fos.fos_quantize_grouped(dev(x), dev(torch.from_numpy(offs)), dev(torch.from_numpy(gam)),
+                                                recipe="4over6")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+    np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+    for bad in ([0, 40, 32, 64, 64], [0, 33, 48, 64, 64], [0, 32, 48, 64, 112]):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        fos.fos_quantize_grouped(dev(x), dev(torch.tensor(bad, dtype=torch.int32)), dev(torch.from_numpy(gam)),
+                                 recipe="4over6", status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) & fos.STATUS_BAD_OFFS
+
+
+# ------------------------------------------------------------------ amax
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_amax(orc, dtype):
+    t = synthdata.activation_family("outlier", 96, 1040, 8, dtype).to(torch.float32)
+    t[3, 5] = float("nan")
+    t[17, :] = float("nan")
+    t[40, 7] = -float("inf") if dtype != "fp16" else -60000.0
+    t = t.to(synthdata.TORCH_DTYPES[dtype])
+    b = raw_bits(t)
+    for gran in ("tensor", "row", "band16"):
+        got = fos.fos_amax(dev(t), gran)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), orc.amax(b, dtype, gran).view(np.uint32))
+
+
+# ------------------------------------------------------------------ boundary
+
+def test_empty_inputs(orc):
+    for M, K in ((0, 64), (8, 0), (0, 0)):
+        x = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        a = torch.ones(1, dtype=torch.float32, device="cuda")
+        codes, scales, sdec = fos.fos_quantize(x, a, recipe="4over6")
+        y = fos.fos_qdq(x, a, recipe="4over6")
+        am = fos.fos_amax(x, "tensor")
+        torch.cuda.synchronize()
+        assert codes.numel() == 0 and y.numel() == 0
+        assert float(am.item()) == 0.0
+        assert float(sdec.item()) == orc.global_decode_scale(1.0, 448)
+
+
+def test_rejects_bad_arguments():
+    x = torch.zeros(16, 64, dtype=torch.bfloat16, device="cuda")
+    a = torch.ones(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(fos.FosError):
+        fos.fos_quantize(torch.zeros(16, 40, dtype=torch.bfloat16, device="cuda"), a)   # K % 16
+    with pytest.raises(fos.FosError):
+        fos.fos_quantize(torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda"), a, block="16x16")  # M % 16
+    with pytest.raises(fos.FosError):
+        fos.fos_quantize(x, a, bound=300)
+    with pytest.raises(fos.FosError):
+        fos.fos_qdq(torch.zeros(16, 64, dtype=torch.float32, device="cuda"), a)  # fp32 QDQ
+    with pytest.raises(fos.FosError):
+        fos.fos_qdq(x, a, block="16x16")
+    flat = torch.zeros(16 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fos.FosError):
+        fos.fos_quantize(flat[1:1 + 16 * 64].view(16, 64), a)  # misaligned
+
+
+def test_runs_on_a_side_stream(orc):
+    x = synthdata.normal(128, 512, 9, "bf16")
+    amax = orc.amax(raw_bits(x), "bf16", "tensor")
+    want = orc.quantize(raw_bits(x), "bf16", amax, recipe="4over6")
+    s = torch.cuda.Stream()
+    xd, ad = dev(x), dev(torch.from_numpy(amax))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        codes, scales, _ = fos.fos_quantize(xd, ad, recipe="4over6")
+    s.synchronize()
+    np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+    np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
