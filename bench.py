@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the four-over-six NVFP4 quantizer on one MI355X.
+
+One step is one pass of the hot path over the dense-activation workload
+(bf16 8192x4096 drawn from N(0,1), 1x16 blocks, per-tensor global scale,
+four-over-six with MSE exact error, E4M3 bound 448): the NaN-dropping tensor
+amax (fos_amax) and the quantize kernel (fos_quantize) writing packed E2M1
+codes and E4M3 scales. Inputs rotate over enough resident copies that the
+footprint exceeds the 256 MB Infinity Cache, so every step reads from HBM.
+
+`value` is the step's algorithmic HBM traffic (amax read 2 B/elem plus
+quantize 2 + 0.5 + 1/16 B/elem) over the measured step time. The `roofline`
+object covers the quantize kernel alone, timed with HIP events on the stream
+it runs on. `cpu_baseline` times the CPU oracle on the same workload. Other
+configurations (16x16 weights, the fused-QDQ expert list, the grouped MoE
+tensor) are timed briefly and reported under `other_workloads`.
+
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public spec
+MALL_BYTES = 256 << 20
+FOOTPRINT = 1 << 30            # rotate buffers up to >= 1 GiB
+METRIC = "4over6 quantize/QDQ achieved HBM GB/s and % of MI355X peak (bit-exact)"
+COUNTERS = os.path.join(ROOT, "profiles", "quantize_1x16_bf16_8192x4096_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_adaptive_block_amd", "csrc", f)
+                  for f in ("fos_kernels.hip", "fos_device.h", "fos_kernels.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_counters():
+    """HBM bytes per quantize launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel code."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def rotating(t, n_bytes_per_set, extra_per_set=0):
+    import torch
+    per = n_bytes_per_set + extra_per_set
+    n = max(2, -(-FOOTPRINT // per))
+    return [t.clone() for _ in range(n)] if t is not None else [None] * n
+
+
+def time_loop(fn, n_sets, steps, warmup):
+    """Run fn(i) for warmup untimed and `steps` timed iterations on the current
+    stream; returns (total_ms, per-launch ms list from events around fn)."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        evs[i][0].record()
+        fn(i % n_sets)
+        evs[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), [a.elapsed_time(b) for a, b in evs]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle sample time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other workloads")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for rocprofv3: a few quantize launches and a known-size copy, no JSON")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "the quantizer has no cross-GPU step here, so multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_adaptive_block_amd as fos
+    import synthdata
+    from synthdata import raw_bits
+
+    torch.cuda.set_device(0)
+    M, K = 8192, 4096
+    n = M * K
+    knobs = dict(recipe="4over6", block="1x16", scale_gran="tensor", err_metric="mse", err_prec="exact", bound=448)
+    log(f"[bench] generating bf16 {M}x{K} N(0,1) (seed 21)")
+    x_host = synthdata.activation_family("normal", M, K, 21, "bf16")
+    x0 = x_host.to("cuda")
+    in_bytes = n * 2
+    out_bytes = n // 2 + n // 16
+    xs = rotating(x0, in_bytes, out_bytes)
+    nset = len(xs)
+    codes = [torch.empty(M, K // 2, dtype=torch.uint8, device="cuda") for _ in range(nset)]
+    scales = [torch.empty(M, K // 16, dtype=torch.uint8, device="cuda") for _ in range(nset)]
+    sdec = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(nset)]
+    amax = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(nset)]
+    log(f"[bench] {nset} rotating buffer sets ({nset * (in_bytes + out_bytes) / 2**30:.2f} GiB)")
+
+    if args.profile_pass:
+        # a few launches of each kernel, plus a plain copy of known size for
+        # calibrating the HBM counters
+        for i in range(8):
+            fos.fos_amax(xs[i % nset], "tensor", out=amax[i % nset])
+            fos.fos_quantize(xs[i % nset], amax[i % nset], codes=codes[i % nset], scales=scales[i % nset],
+                             sdec=sdec[i % nset], **knobs)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] profile pass done (copy kernel: 268435456 bytes read and written per launch)")
+        return
+
+    # ---------------------------------------------------------------- main step
+    def step(i, evs=None):
+        if evs is not None:
+            evs[0].record()
+        fos.fos_amax(xs[i], "tensor", out=amax[i])
+        if evs is not None:
+            evs[1].record()
+        fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)
+        if evs is not None:
+            evs[2].record()
+
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    for i in range(args.warmup):
+        step(i % nset)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step((args.warmup + i) % nset, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    a_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    q_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = total_ms / args.steps
+    q_avg_ms = float(np.mean(q_ms))
+    a_avg_ms = float(np.mean(a_ms))
+    step_bytes = n * 2 + n * 2 + out_bytes          # amax read + quantize read + write
+    q_bytes = in_bytes + out_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    q_gbs = q_bytes / (q_avg_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s); quantize {q_avg_ms * 1e3:.1f} us "
+        f"({q_gbs:.0f} GB/s, {q_gbs / PEAK_HBM_GBS:.1%} of peak); amax {a_avg_ms * 1e3:.1f} us")
+
+    # bit-exact spot check of the last outputs against the CPU oracle
+    bit_exact = None
+    try:
+        import oracle
+        orc = oracle.get()
+        last = (args.warmup + args.steps - 1) % nset
+        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(0).integers(0, M, 62)]))
+        a_host = orc.amax(raw_bits(x_host), "bf16", "tensor")
+        want = orc.quantize(raw_bits(x_host)[rows], "bf16", a_host, **knobs)
+        got_c = codes[last].cpu().numpy()[rows]
+        got_s = scales[last].cpu().numpy()[rows]
+        got_a = amax[last].cpu().numpy()
+        bit_exact = bool(np.array_equal(got_c, want["codes"]) and np.array_equal(got_s, want["scales"])
+                         and got_a.view(np.uint32)[0] == a_host.view(np.uint32)[0])
+        log(f"[bench] bit-exact vs oracle on {rows.size} sampled rows and the amax: {bit_exact}")
+    except Exception as e:  # the oracle is optional for timing
+        log(f"[bench] oracle spot check skipped: {e}")
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        xb = raw_bits(x_host)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            a_h = orc.amax(xb, "bf16", "tensor")
+            orc.quantize(xb, "bf16", a_h, **knobs)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el > 30:
+                break
+        cpu = {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+               "kind": "oracle",
+               "sample": f"{reps} full steps (amax + quantize of the whole bf16 {M}x{K} tensor) in {el:.1f} s"}
+        log(f"[bench] CPU oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    # ---------------------------------------------------------------- other workloads
+    other = {}
+    if not args.no_other:
+        other = other_workloads(fos, synthdata, torch, np)
+
+    traffic = read_counters()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "dense activation quantize, bf16 8192x4096 N(0,1) seed 21, 1x16 blocks, "
+                               "per-tensor amax (fos_amax) + four-over-six MSE exact, E4M3 bound 448",
+                   "M": M, "K": K, "input_dtype": "bf16", "recipe": "4over6", "err_metric": "mse",
+                   "err_prec": "exact", "e4m3_bound": 448, "rotating_sets": nset,
+                   "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "fos_quantize (k_1x16, bf16, 4over6 MSE exact)",
+                     "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(q_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": q_bytes, "avg_launch_us": round(q_avg_ms * 1e3, 2)},
+        "amax_kernel": {"avg_launch_us": round(a_avg_ms * 1e3, 2),
+                        "achieved_GBs": round(in_bytes / (a_avg_ms * 1e-3) / 1e9, 1)},
+        "bit_exact_sample": bit_exact,
+        "cpu_baseline": cpu,
+        "other_workloads": other,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def other_workloads(fos, synthdata, torch, np, steps=50, warmup=5):
+    """Brief kernel-only timings of the other configurations (precomputed amax)."""
+    out = {}
+
+    def gbs(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    # 16x16 weights, bf16 4096x14336 and fp32 4096x4096, per-tensor, MSE exact, 448
+    for dtype, (M, K) in (("bf16", (4096, 14336)), ("fp32", (4096, 4096))):
+        w = synthdata.weight(M, K, 31, dtype).to("cuda")
+        a = fos.fos_amax(w, "tensor")
+        eb = 2 if dtype == "bf16" else 4
+        nbytes = M * K * eb + M * K // 2 + M * K // 16
+        ws = rotating(w, nbytes)
+        c = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+        s = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
+        sd = torch.empty(1, dtype=torch.float32, device="cuda")
+        _, ms = time_loop(lambda i: fos.fos_quantize(ws[i], a, codes=c, scales=s, sdec=sd, recipe="4over6",
+                                                     block="16x16", err_metric="mse", err_prec="exact"),
+                          len(ws), steps, warmup)
+        avg = float(np.mean(ms))
+        out[f"quantize_16x16_{dtype}_{M}x{K}"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
+                                                  "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
+        log(f"[bench] 16x16 {dtype} {M}x{K}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
+        del ws, w
+
+    # fused QDQ over 8 expert weights 2048x7168, bf16 and fp16, the five timed modes
+    lst = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=("bf16", "fp16"))
+    for dtype in ("bf16", "fp16"):
+        xs = [t.to("cuda") for t in lst[dtype]]
+        ams = [fos.fos_amax(t, "tensor") for t in xs]
+        ys = [torch.empty_like(t) for t in xs]
+        nbytes = sum(t.numel() for t in xs) * 4
+        for mode in (("nvfp4", "mse", "fp16", 448), ("4over6", "mae", "fp16", 448), ("4over6", "mae", "fp16", 256),
+                     ("4over6", "mse", "fp16", 448), ("4over6", "mse", "fp16", 256)):
+            r, m, p, bnd = mode
+            _, ms = time_loop(lambda i: fos.fos_qdq_list(xs, ams, outs=ys, recipe=r, err_metric=m, err_prec=p,
+                                                         bound=bnd), 1, steps, warmup)
+            avg = float(np.mean(ms))
+            key = f"qdq_list_8x2048x7168_{dtype}_{r}" + ("" if r == "nvfp4" else f"_{m}_{p}_{bnd}")
+            out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
+                        "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
+            log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
+        del xs, ys
+    del lst
+
+    # grouped MoE activations: 65536 (+4096 padding) x 7168, 64 groups, MSE exact
+    M, pad, K, G = 65536, 4096, 7168, 64
+    x, offs, fac = synthdata.grouped_tokens(M, pad, K, G)
+    x = x.to("cuda")
+    offs_d = torch.from_numpy(offs).to("cuda")
+    starts = np.concatenate([[0], offs[:-1]])
+    gam = torch.stack([fos.fos_amax(x[s:e].contiguous(), "tensor")[0] if e > s else
+                       torch.zeros((), device="cuda") for s, e in zip(starts, offs)])
+    c = torch.empty(M + pad, K // 2, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M + pad, K // 16, dtype=torch.uint8, device="cuda")
+    nbytes = M * K * 2 + (M + pad) * (K // 2 + K // 16)
+    for bnd in (448, 256):
+        _, ms = time_loop(lambda i: fos.fos_quantize_grouped(x, offs_d, gam, codes=c, scales=s, recipe="4over6",
+                                                             err_metric="mse", err_prec="exact", bound=bnd),
+                          1, steps, warmup)
+        avg = float(np.mean(ms))
+        key = f"quantize_grouped_{M}+{pad}x{K}_G{G}_{bnd}"
+        out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
+                    "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
+        log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
+    return out
+
+
+if __name__ == "__main__":
+    main()

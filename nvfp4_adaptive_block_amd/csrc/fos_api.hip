@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <algorithm>
 
 #include "fos.h"
 #include "fos_kernels.h"
@@ -139,7 +140,10 @@ int fos_amax(const void* x, int dtype, int64_t M, int64_t K, int gran, float* am
   if (M * K == 0)  // no elements: every amax is +0
     return launch_status(fos::launch_zero_u32(amax_out, gran == FOS_AMAX_TENSOR ? 1 : M, s));
   const int64_t n16 = M * K / 16;
-  int grid = grid_for(gran == FOS_AMAX_TENSOR ? (n16 + 63) / 64 : M);
+  // per tensor: at most 256 workgroups, so that their same-address atomics
+  // (which serialize at the memory side) stay few
+  int grid = gran == FOS_AMAX_TENSOR ? (int)std::max<int64_t>(1, std::min<int64_t>(256, (n16 + 1023) / 1024))
+                                     : grid_for(M);
   return launch_status(fos::launch_amax(dtype, gran, x, M, K, amax_out, grid, s));
 }
 
@@ -159,21 +163,23 @@ int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* am
   int metric, prec;
   mode_of(cfg, metric, prec);
   const bool per_row = cfg->scale_gran == FOS_PER_ROW;
-  if (sdec_out && (per_row ? M : 1) > 0)
-    if ((rc = launch_status(fos::launch_sdec(amax, per_row ? M : 1, six_b(cfg), sdec_out, s)))) return rc;
-  if (M * K == 0) return FOS_OK;
+  // the kernels also write S_dec; with no elements only S_dec remains
+  if (M * K == 0 && !(sdec_out && (per_row ? M : 1) > 0)) return FOS_OK;
   if (cfg->block == FOS_BLOCK_1X16) {
     fos::Args1x16<1> a;
     memset(&a, 0, sizeof a);
-    a.t[0] = fos::TensorRef{x, nullptr, amax, M, K, 0};
+    a.t[0] = fos::TensorRef{x, nullptr, amax, M, K > 0 ? K : 16, 0};
     a.n = 1;
-    a.total_units = (M * (K / 16) + 63) / 64;
+    // units: 64 blocks of the flattened tensor, or per-row segments of up to
+    // 64 blocks (one global scale per unit)
+    const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
+    a.total_units = per_row ? M * ((K / 16 + ub - 1) / ub) : (M * (K / 16) + ub - 1) / ub;
     a.six_b = six_b(cfg);
     a.codes = codes;
     a.scales = scales;
+    a.sdec_out = sdec_out;
     return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec,
-                                                per_row ? fos::kGranRow : fos::kGranTensor, a,
-                                                grid_for(a.total_units), s));
+                                                per_row ? fos::kGranRow : fos::kGranTensor, a, s));
   }
   fos::Args16x16 a;
   a.x = x;
@@ -184,10 +190,10 @@ int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* am
   a.six_b = six_b(cfg);
   a.codes = codes;
   a.scales = scales;
+  a.sdec_out = sdec_out;
   a.status = d_status;
-  const int64_t units = (M / 16) * ((K / 16 + 3) / 4);
   return launch_status(fos::launch_quant_16x16(dtype, cfg->recipe, metric, prec,
-                                               per_row ? fos::kGranRow : fos::kGranTensor, a, grid_for(units), s));
+                                               per_row ? fos::kGranRow : fos::kGranTensor, a, s));
 }
 
 static int check_qdq_cfg(const fos_config* cfg, int dtype) {
@@ -226,12 +232,12 @@ int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_confi
       const fos_tensor_desc& d = descs[i];
       if (d.M * d.K == 0) continue;
       a.t[a.n++] = fos::TensorRef{d.x, d.y, d.amax, d.M, d.K, units};
-      units += (d.M * (d.K / 16) + 63) / 64;
+      units += (d.M * (d.K / 16) + fos::unit_blocks(fos::kOutQdq, dtype) - 1) / fos::unit_blocks(fos::kOutQdq, dtype);
     }
     if (a.n == 0) continue;
     a.total_units = units;
     a.six_b = six_b(cfg);
-    if ((rc = launch_status(fos::launch_qdq_1x16(dtype, cfg->recipe, metric, prec, a, grid_for(units), s)))) return rc;
+    if ((rc = launch_status(fos::launch_qdq_1x16(dtype, cfg->recipe, metric, prec, a, s)))) return rc;
   }
   return FOS_OK;
 }
@@ -276,24 +282,21 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   int metric, prec;
   mode_of(cfg, metric, prec);
-  if (d_status)
-    if ((rc = launch_status(fos::launch_check_offs(offs, G, M_alloc, d_status, s)))) return rc;
-  if (group_sdec_out)
-    if ((rc = launch_status(fos::launch_sdec(group_amax, G, six_b(cfg), group_sdec_out, s)))) return rc;
-  if (M_alloc * K == 0) return FOS_OK;
   fos::Args1x16<1> a;
   memset(&a, 0, sizeof a);
-  a.t[0] = fos::TensorRef{x, nullptr, nullptr, M_alloc, K, 0};
+  a.t[0] = fos::TensorRef{x, nullptr, nullptr, M_alloc, K > 0 ? K : 16, 0};
   a.n = 1;
   a.G = G;
-  a.total_units = (M_alloc * (K / 16) + 63) / 64;
+  const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
+  a.total_units = M_alloc * ((K / 16 + ub - 1) / ub);  // per-row segments
   a.six_b = six_b(cfg);
   a.codes = codes;
   a.scales = scales;
+  a.sdec_out = group_sdec_out;
+  a.status = d_status;
   a.offs = offs;
   a.group_amax = group_amax;
-  return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, fos::kGranGroup, a,
-                                              grid_for(a.total_units), s));
+  return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, fos::kGranGroup, a, s));
 }
 
 }  // extern "C"

@@ -111,6 +111,25 @@ __device__ __forceinline__ void e2m1_unpack8(uint32_t w, float* out) {
   out[4] = c.x; out[5] = c.y; out[6] = d.x; out[7] = d.y;
 }
 
+// ---------------------------------------------------------------- division
+
+// RN(a / 6) for a >= 0 (or NaN): a product with RN(1/6) corrected by one
+// fused multiply-add of the exact remainder. Checked exhaustively on every
+// non-negative binary32 input: it is correctly rounded except where the
+// quotient is subnormal (a < 2^-125), which takes the division instead.
+__device__ __forceinline__ float div6(float a) {
+  constexpr float r6 = 0x1.555556p-3f;  // RN(1/6)
+  const float q0 = a * r6;
+  const float r = __builtin_fmaf(-q0, 6.0f, a);
+  float q = __builtin_fmaf(r, r6, q0);
+  if (__ballot(a < 0x1p-125f)) q = (a < 0x1p-125f) ? a / 6.0f : q;
+  return q;
+}
+
+// RN(x - f32(RN16(xh))): the error of x against the decoded value rounded to
+// binary16 (FP16-error mode).
+__device__ __forceinline__ float sub_f16(float x, float xh) { return x - round_f16(xh); }
+
 // ---------------------------------------------------------------- reductions
 
 // The pinned width-16 order: strides 8, 4, 2, 1 where position i adds

@@ -21,6 +21,15 @@ enum { kStatusTileNonuniform = 1, kStatusBadOffs = 2 };
 // kernel arguments, 48 B each).
 constexpr int kMaxList = 48;
 
+// 16-element blocks per lane in one unit of the 1x16 kernels: a unit is
+// 64 * NB consecutive blocks of a row (per-row and grouped scales) or of the
+// flattened tensor (per-tensor scale). Quantizing 16-bit inputs keeps two
+// blocks per lane in flight; fp32 inputs (twice the registers per block) and
+// the fused QDQ (which holds decoded values too) keep one.
+__host__ __device__ constexpr int unit_blocks(int out, int dt) {
+  return 64 * ((out == kOutQuant && dt != kFP32) ? 2 : 1);
+}
+
 // One tensor of a 1x16 launch. unit_begin: index of its first 64-block unit
 // in the launch's unit space.
 struct TensorRef {
@@ -40,6 +49,8 @@ struct Args1x16 {
   float six_b;      // 6 * E4M3 bound
   uint8_t* codes;   // quantize outputs (single tensor)
   uint8_t* scales;
+  float* sdec_out;  // nullable: S_dec per tensor [1], row [M] or group [G]
+  int32_t* status;  // nullable device status word
   const int32_t* offs;       // grouped: cumulative end offsets [G]
   const float* group_amax;   // grouped: [G]
 };
@@ -52,20 +63,17 @@ struct Args16x16 {
   float six_b;
   uint8_t* codes;
   uint8_t* scales;
+  float* sdec_out;  // nullable: S_dec per tensor [1] or row [M]
   int32_t* status;
 };
 
-hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a, int grid,
+hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a,
                              hipStream_t s);
-hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, int grid,
-                           hipStream_t s);
-hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, int grid,
-                              hipStream_t s);
+hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, hipStream_t s);
+hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, hipStream_t s);
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,
                           int64_t M, int64_t K, void* y, int grid, hipStream_t s);
 hipError_t launch_amax(int dt, int gran, const void* x, int64_t M, int64_t K, float* out, int grid, hipStream_t s);
-hipError_t launch_sdec(const float* amax, int64_t n, float six_b, float* out, hipStream_t s);
 hipError_t launch_zero_u32(void* p, int64_t n, hipStream_t s);
-hipError_t launch_check_offs(const int32_t* offs, int G, int64_t M_alloc, int32_t* status, hipStream_t s);
 
 }  // namespace fos

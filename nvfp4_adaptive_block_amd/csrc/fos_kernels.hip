@@ -11,90 +11,220 @@
 // writes only BF16/FP16, list API, E4M3 bound 448/256, MAE/MSE, exact or
 // FP16 candidate error; static dispatch of every mode).
 //
-// Work mapping (1x16 blocks): one lane owns one 16-element block, so the
+// Work mapping, 1x16 blocks: one lane owns one 16-element block, so the
 // block amax, both candidates, the 16-term error tree and the selection stay
-// in that lane's registers; a wave covers 64 consecutive blocks (2 KiB of
-// bf16, read with 128-bit loads) and walks a contiguous range of such units,
-// so per-row global scales are recomputed only when a lane's row changes.
-// 16x16 tiles: a lane owns one 16-element row segment of a tile, 16 lanes
-// (one DPP row) hold a tile, and the tile amax and error sums cross lanes.
+// in that lane's registers. A wave covers a unit of 64 consecutive blocks
+// (2 KiB of bf16 read with 128-bit loads) and walks a contiguous range of
+// units, loading the next unit while it computes the current one. The grid
+// holds only as many workgroups as are resident at once.
+//
+// Per-block division is replaced by a table: the block scale sigma is one of
+// 127 E4M3 values, so for each global scale the wave keeps, in LDS, the
+// encode multipliers RN(S_enc / sigma) and decode multipliers
+// RN(sigma * S_dec) of all 127 codes, rebuilt when the wave's tensor (or
+// row) changes. A unit whose lanes straddle rows of different global scales
+// divides per lane instead.
+//
+// 16x16 tiles: a lane owns one 16-element row segment of a tile, the 16 lanes
+// of a DPP row hold the tile's rows, and the tile amax and error sums cross
+// lanes. A unit is one 16-row band times four tiles.
 #include "fos_device.h"
 #include "fos_kernels.h"
 
 namespace fos {
 
-// ------------------------------------------------------------ loads/stores
+// ------------------------------------------------------------ memory
 
-template <int DT> struct Io;
+// Raw buffer loads and stores. A lane whose offset lies past the resource's
+// range reads zeros and its stores are dropped by the hardware, so ragged
+// tails and idle lanes need no branch around memory operations (which would
+// make the compiler wait for every outstanding load, prefetches included).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource
 
-template <> struct Io<kBF16> {
-  static constexpr int kBytes = 2;
-  __device__ static void load16(const void* base, int64_t idx, float* x) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    uint4 a = p[0], b = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// A block's raw bits, loaded ahead of use.
+template <int DT> struct Raw;
+
+template <> struct Raw<kBF16> {
+  static constexpr int kBytes = 32;  // bytes of one 16-element block
+  v4i a, b;
+  __device__ void load(Rsrc r, uint32_t off) {
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+  }
+  __device__ void unpack(float* x) const {
+    const uint32_t w[8] = {(uint32_t)a.x, (uint32_t)a.y, (uint32_t)a.z, (uint32_t)a.w,
+                           (uint32_t)b.x, (uint32_t)b.y, (uint32_t)b.z, (uint32_t)b.w};
 #pragma unroll
     for (int i = 0; i < 8; i++) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
   }
-  __device__ static void store16(void* base, int64_t idx, const float* y) {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx);
-    uint4 a, b;
-    a.x = pack_bf16(y[0], y[1]); a.y = pack_bf16(y[2], y[3]); a.z = pack_bf16(y[4], y[5]); a.w = pack_bf16(y[6], y[7]);
-    b.x = pack_bf16(y[8], y[9]); b.y = pack_bf16(y[10], y[11]); b.z = pack_bf16(y[12], y[13]); b.w = pack_bf16(y[14], y[15]);
-    p[0] = a;
-    p[1] = b;
-  }
 };
 
-template <> struct Io<kFP16> {
-  static constexpr int kBytes = 2;
-  __device__ static void load16(const void* base, int64_t idx, float* x) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    uint4 a = p[0], b = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+template <> struct Raw<kFP16> {
+  static constexpr int kBytes = 32;
+  v4i a, b;
+  __device__ void load(Rsrc r, uint32_t off) {
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+  }
+  __device__ void unpack(float* x) const {
+    const uint32_t w[8] = {(uint32_t)a.x, (uint32_t)a.y, (uint32_t)a.z, (uint32_t)a.w,
+                           (uint32_t)b.x, (uint32_t)b.y, (uint32_t)b.z, (uint32_t)b.w};
 #pragma unroll
     for (int i = 0; i < 8; i++) { x[2 * i] = f16_lo(w[i]); x[2 * i + 1] = f16_hi(w[i]); }
   }
-  __device__ static void store16(void* base, int64_t idx, const float* y) {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx);
-    uint4 a, b;
-    a.x = pack_f16(y[0], y[1]); a.y = pack_f16(y[2], y[3]); a.z = pack_f16(y[4], y[5]); a.w = pack_f16(y[6], y[7]);
-    b.x = pack_f16(y[8], y[9]); b.y = pack_f16(y[10], y[11]); b.z = pack_f16(y[12], y[13]); b.w = pack_f16(y[14], y[15]);
-    p[0] = a;
-    p[1] = b;
+};
+
+template <> struct Raw<kFP32> {
+  static constexpr int kBytes = 64;
+  v4i v[4];
+  __device__ void load(Rsrc r, uint32_t off) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+  }
+  __device__ void unpack(float* x) const {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[4 * i] = __int_as_float(v[i].x); x[4 * i + 1] = __int_as_float(v[i].y);
+      x[4 * i + 2] = __int_as_float(v[i].z); x[4 * i + 3] = __int_as_float(v[i].w);
+    }
   }
 };
 
-template <> struct Io<kFP32> {
-  static constexpr int kBytes = 4;
-  __device__ static void load16(const void* base, int64_t idx, float* x) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+// Store 16 decoded values as the tensor's element type.
+template <int DT> __device__ __forceinline__ void store16(Rsrc r, uint32_t off, const float* y);
+
+template <> __device__ __forceinline__ void store16<kBF16>(Rsrc r, uint32_t off, const float* y) {
+  const v4i a = {(int)pack_bf16(y[0], y[1]), (int)pack_bf16(y[2], y[3]), (int)pack_bf16(y[4], y[5]),
+                 (int)pack_bf16(y[6], y[7])};
+  const v4i b = {(int)pack_bf16(y[8], y[9]), (int)pack_bf16(y[10], y[11]), (int)pack_bf16(y[12], y[13]),
+                 (int)pack_bf16(y[14], y[15])};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, 0);
+}
+template <> __device__ __forceinline__ void store16<kFP16>(Rsrc r, uint32_t off, const float* y) {
+  const v4i a = {(int)pack_f16(y[0], y[1]), (int)pack_f16(y[2], y[3]), (int)pack_f16(y[4], y[5]),
+                 (int)pack_f16(y[6], y[7])};
+  const v4i b = {(int)pack_f16(y[8], y[9]), (int)pack_f16(y[10], y[11]), (int)pack_f16(y[12], y[13]),
+                 (int)pack_f16(y[14], y[15])};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, 0);
+}
+template <> __device__ __forceinline__ void store16<kFP32>(Rsrc r, uint32_t off, const float* y) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      float4 v = p[i];
-      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-    }
+  for (int i = 0; i < 4; i++) {
+    const v4i a = {__float_as_int(y[4 * i]), __float_as_int(y[4 * i + 1]), __float_as_int(y[4 * i + 2]),
+                   __float_as_int(y[4 * i + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * i, 0, 0);
   }
-  __device__ static void store16(void* base, int64_t idx, const float* y) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
+}
+
+__device__ __forceinline__ void store_codes(Rsrc r, uint32_t off, uint32_t c0, uint32_t c1) {
+  const v2i v = {(int)c0, (int)c1};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store_scale(Rsrc r, uint32_t off, uint32_t s) {
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)s, r, off, 0, 0);
+}
+
+// Stores that touch nothing (zero-range resource), fenced against
+// reordering: between the first unit's loads and the second unit's, they
+// stand in for the stores a loop iteration issues there (two per block), so that the
+// compiler's memory wait before the first use equals the loop's.
+template <int NB>
+__device__ __forceinline__ void dummy_stores() {
+  __builtin_amdgcn_sched_barrier(0);
+  const Rsrc none = make_rsrc(nullptr, 0);
 #pragma unroll
-    for (int i = 0; i < 4; i++) p[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+  for (int j = 0; j < NB; j++) {
+    store_codes(none, 0, 0u, 0u);
+    store_scale(none, 0, 0u);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Loads of values no kernel writes (amaxes, offsets), from the constant
+// address space so that wave-uniform addresses become scalar loads.
+typedef __attribute__((address_space(4))) const float* ConstF32;
+typedef __attribute__((address_space(4))) const int32_t* ConstI32;
+__device__ __forceinline__ float ld_const(const float* p, int64_t i) {
+  return ((ConstF32)(const void*)p)[i];
+}
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, int64_t i) {
+  return ((ConstI32)(const void*)p)[i];
+}
+
+// ------------------------------------------------------------ scales
+
+// Per-wave LDS table of the multipliers of all E4M3 codes for one global
+// scale: E[c] = RN(S_enc / sigma_c) (0 for sigma = 0, FLT_MAX on overflow),
+// D[c] = RN(sigma_c * S_dec). Codes never exceed 0x7E (scales saturate).
+struct Table {
+  float* E;
+  float* D;
+  __device__ void build(float S_enc, float S_dec, int lane) const {
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int c = lane + 64 * k;
+      const float sigma = e4m3_value((uint32_t)c);
+      const bool zero = sigma == 0.0f || c >= 0x7F;
+      const float e = S_enc / (zero ? 1.0f : sigma);
+      E[c] = zero ? 0.0f : __builtin_fminf(e, kFltMax);
+      D[c] = (c >= 0x7F) ? 0.0f : sigma * S_dec;
+    }
+    // the lanes of this wave read what other lanes wrote
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 };
+
+// One candidate's block scale and multipliers: t = RN(q * S_enc) with q the
+// already divided block amax (RN(a/6) or RN(a/4)); scale = E4M3(t). With
+// TAB the multipliers come from the wave's table, otherwise they are
+// computed here with correctly rounded division.
+struct Cand {
+  uint32_t scale;
+  float E, D;
+};
+
+template <bool TAB>
+__device__ __forceinline__ Cand make_cand(float q, float S_enc, float S_dec, const Table& tab) {
+  Cand c;
+  c.scale = e4m3_code(q * S_enc);
+  if (TAB) {
+    c.E = tab.E[c.scale];
+    c.D = tab.D[c.scale];
+  } else {
+    const float sigma = e4m3_value(c.scale);
+    const bool zero = sigma == 0.0f;
+    const float e = S_enc / (zero ? 1.0f : sigma);
+    c.E = zero ? 0.0f : __builtin_fminf(e, kFltMax);
+    c.D = sigma * S_dec;
+  }
+  return c;
+}
 
 // ------------------------------------------------------------ block pieces
 
-// NaN-dropping max |x| over 16 values. The fast form uses v_max3_f32, which
-// is exact whenever no element is NaN; a block holding a NaN is always
-// recomputed by the careful form (integer max over the magnitude bits with
-// NaN patterns mapped to +0).
+// NaN-dropping max |x| over 16 values. The fast form (v_max3_f32) is exact
+// whenever no element is NaN; a block holding a NaN is always recomputed by
+// the careful form (integer max over the magnitude bits, NaN patterns -> +0).
 template <bool CAREFUL>
 __device__ __forceinline__ float amax16(const float* x) {
   if (CAREFUL) {
     uint32_t a = 0;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      uint32_t m = __float_as_uint(x[i]) & 0x7FFFFFFFu;
+      const uint32_t m = __float_as_uint(x[i]) & 0x7FFFFFFFu;
       a = max(a, m <= 0x7F800000u ? m : 0u);
     }
     return __uint_as_float(a);
@@ -112,27 +242,6 @@ __device__ __forceinline__ bool any_nan16(const float* x) {
 #pragma unroll
   for (int i = 1; i < 16; i++) m = __builtin_elementwise_maximum(m, x[i]);
   return m != m;
-}
-
-// One candidate's block scale and multipliers: t = RN(q * S_enc) with q the
-// already divided amax (RN(a/6) or RN(a/4)); scale = E4M3(t); encode
-// multiplier E = RN(S_enc / sigma) (0 for sigma = 0, FLT_MAX on overflow);
-// decode multiplier D = RN(sigma * S_dec).
-struct Cand {
-  uint32_t scale;
-  float E, D;
-};
-
-__device__ __forceinline__ Cand make_cand(float q, float S_enc, float S_dec) {
-  Cand c;
-  float t = q * S_enc;
-  c.scale = e4m3_code(t);
-  float sigma = e4m3_value(c.scale);
-  bool zero = sigma == 0.0f;
-  float e = S_enc / (zero ? 1.0f : sigma);
-  c.E = zero ? 0.0f : __builtin_fminf(e, kFltMax);
-  c.D = sigma * S_dec;
-  return c;
 }
 
 // E2M1 codes of x * E. The careful form encodes NaN elements as +6.
@@ -163,51 +272,54 @@ __device__ __forceinline__ float err16(const float* x, const float* xh) {
   float u[16];
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    float r = (PREC == kErrFP16) ? round_f16(xh[i]) : xh[i];
-    float e = x[i] - r;
+    const float e = (PREC == kErrFP16) ? sub_f16(x[i], xh[i]) : x[i] - xh[i];
     u[i] = (METRIC == kMAE) ? __builtin_fabsf(e) : e * e;
   }
   return tree16(u);
 }
 
-// Everything a kernel needs to store for one block (or one tile row).
 struct BlockOut {
   uint32_t c0, c1;  // 16 E2M1 codes
   uint32_t scale;   // E4M3 code
-  float D;          // decode multiplier of the kept candidate
 };
 
 // Quantize one 1x16 block held in x. When NEED_XHAT, xh receives the kept
 // candidate's decoded values. Returns false when the fast form cannot be
 // trusted (the block holds a NaN); the caller then reruns with CAREFUL.
-template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT>
-__device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_dec, BlockOut& o, float* xh) {
+template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, bool TAB>
+__device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_dec, const Table& tab, BlockOut& o,
+                                           float* xh) {
   const float a = amax16<CAREFUL>(x);
-  const Cand k6 = make_cand(a / 6.0f, S_enc, S_dec);
+  const Cand k6 = make_cand<TAB>(div6(a), S_enc, S_dec, tab);
   uint32_t c60, c61;
   encode16<CAREFUL>(x, k6.E, c60, c61);
   if (RECIPE == kNVFP4) {
-    o.c0 = c60; o.c1 = c61; o.scale = k6.scale; o.D = k6.D;
+    o.c0 = c60; o.c1 = c61; o.scale = k6.scale;
     if (NEED_XHAT) decode16(c60, c61, k6.D, xh);
     return CAREFUL || !any_nan16(x);
   } else {
-    const Cand k4 = make_cand(a * 0.25f, S_enc, S_dec);
+    float e6;
+    {
+      float t[16];
+      decode16(c60, c61, k6.D, t);
+      e6 = err16<METRIC, PREC>(x, t);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const Cand k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
     uint32_t c40, c41;
     encode16<CAREFUL>(x, k4.E, c40, c41);
-    float xh6[16], xh4[16];
-    decode16(c60, c61, k6.D, xh6);
-    decode16(c40, c41, k4.D, xh4);
-    const float e6 = err16<METRIC, PREC>(x, xh6);
-    const float e4 = err16<METRIC, PREC>(x, xh4);
+    float e4;
+    {
+      float t[16];
+      decode16(c40, c41, k4.D, t);
+      e4 = err16<METRIC, PREC>(x, t);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const bool four = e4 < e6;
     o.c0 = four ? c40 : c60;
     o.c1 = four ? c41 : c61;
     o.scale = four ? k4.scale : k6.scale;
-    o.D = four ? k4.D : k6.D;
-    if (NEED_XHAT) {
-#pragma unroll
-      for (int i = 0; i < 16; i++) xh[i] = four ? xh4[i] : xh6[i];
-    }
+    if (NEED_XHAT) decode16(o.c0, o.c1, four ? k4.D : k6.D, xh);
     return CAREFUL || (e6 == e6 && e4 == e4);
   }
 }
@@ -217,20 +329,21 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
 // amax is the max over the lanes; each lane sums its row's error terms with
 // the pinned tree, and the lane sums are combined with the same tree in row
 // order. The result (kept candidate) is the same on all 16 lanes.
-template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT>
-__device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_dec, BlockOut& o, float* xh) {
+template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, bool TAB>
+__device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_dec, const Table& tab, BlockOut& o,
+                                           float* xh) {
   const float a = max16_lanes(amax16<CAREFUL>(x));
-  const Cand k6 = make_cand(a / 6.0f, S_enc, S_dec);
+  const Cand k6 = make_cand<TAB>(div6(a), S_enc, S_dec, tab);
   uint32_t c60, c61;
   encode16<CAREFUL>(x, k6.E, c60, c61);
   if (RECIPE == kNVFP4) {
-    o.c0 = c60; o.c1 = c61; o.scale = k6.scale; o.D = k6.D;
+    o.c0 = c60; o.c1 = c61; o.scale = k6.scale;
     if (NEED_XHAT) decode16(c60, c61, k6.D, xh);
     if (CAREFUL) return true;
-    float n = any_nan16(x) ? 1.0f : 0.0f;
+    const float n = any_nan16(x) ? 1.0f : 0.0f;
     return max16_lanes(n) == 0.0f;
   } else {
-    const Cand k4 = make_cand(a * 0.25f, S_enc, S_dec);
+    const Cand k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
     uint32_t c40, c41;
     encode16<CAREFUL>(x, k4.E, c40, c41);
     float xh6[16], xh4[16];
@@ -244,7 +357,6 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
     o.c0 = four ? c40 : c60;
     o.c1 = four ? c41 : c61;
     o.scale = four ? k4.scale : k6.scale;
-    o.D = four ? k4.D : k6.D;
     if (NEED_XHAT) {
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = four ? xh4[i] : xh6[i];
@@ -253,103 +365,220 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
   }
 }
 
-__device__ __forceinline__ void store_codes(uint8_t* codes, int64_t byte_idx, uint32_t c0, uint32_t c1) {
-  *reinterpret_cast<uint2*>(codes + byte_idx) = make_uint2(c0, c1);
+// Quantize a 1x16 block with the fast form, falling back to the careful form
+// when the block holds a NaN.
+template <int RECIPE, int METRIC, int PREC, bool NEED_XHAT, bool TAB>
+__device__ __forceinline__ void quantize_block(const float* x, float S_enc, float S_dec, const Table& tab,
+                                               BlockOut& o, float* xh) {
+  if (!block_1x16<RECIPE, METRIC, PREC, false, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh))
+    block_1x16<RECIPE, METRIC, PREC, true, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh);
 }
 
 // ------------------------------------------------------------ 1x16 kernel
 
-// Lane position inside a tensor: (row, column block), advanced by 64 blocks
-// per unit.
-struct Pos {
-  int64_t row, cb;
-};
-
-__device__ __forceinline__ Pos pos_of(int64_t b, int64_t nbk) { return Pos{b / nbk, b % nbk}; }
-
-__device__ __forceinline__ void advance(Pos& p, int64_t nbk, int64_t dr, int64_t dc) {
-  p.row += dr;
-  p.cb += dc;
-  if (p.cb >= nbk) { p.cb -= nbk; p.row += 1; }
-}
-
 // Row -> group through the cumulative end offsets (binary search: the first
-// g with r < offs[g]); G >= 1 and r < offs[G-1].
+// g with r < offs[g]; rows past offs[G-1] map to G-1). Wave-uniform.
 __device__ __forceinline__ int group_of(const int32_t* offs, int G, int64_t r) {
   int lo = 0, hi = G - 1;
   while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (r < (int64_t)offs[mid]) hi = mid; else lo = mid + 1;
+    const int mid = (lo + hi) >> 1;
+    if (r < (int64_t)ld_const(offs, mid)) hi = mid; else lo = mid + 1;
   }
   return lo;
 }
 
+// S_dec side outputs and the offsets check, spread over the grid.
+template <int GRAN, int NT>
+__device__ void side_outputs(const Args1x16<NT>& args) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gsz = (int64_t)gridDim.x * blockDim.x;
+  if (args.sdec_out) {
+    if (GRAN == kGranTensor) {
+      if (gid == 0) args.sdec_out[0] = 1.0f / global_encode_scale(args.t[0].amax[0], args.six_b);
+    } else if (GRAN == kGranRow) {
+      for (int64_t r = gid; r < args.t[0].M; r += gsz)
+        args.sdec_out[r] = 1.0f / global_encode_scale(args.t[0].amax[r], args.six_b);
+    } else {
+      for (int64_t g = gid; g < args.G; g += gsz)
+        args.sdec_out[g] = 1.0f / global_encode_scale(args.group_amax[g], args.six_b);
+    }
+  }
+  if (GRAN == kGranGroup && args.status) {
+    for (int64_t g = gid; g < args.G; g += gsz) {
+      const int32_t prev = g ? args.offs[g - 1] : 0;
+      const int32_t o = args.offs[g];
+      const bool bad = o < prev || (o & 15) || (g == args.G - 1 && (int64_t)o > args.t[0].M);
+      if (bad) atomicOr(args.status, kStatusBadOffs);
+    }
+  }
+}
+
+// The buffer resources of one unit of a 1x16 launch.
+struct Unit {
+  Rsrc x, out, scl;  // input, codes (or QDQ output), scales
+};
+
+// Units of a 1x16 launch. Per-tensor scales: a unit is 64 consecutive blocks
+// of the flattened tensor. Per-row scales (and grouped): a unit is a segment
+// of up to 64 blocks of one row, so each unit has one global scale.
+// Position of a unit: its index in the tensor and, for per-row units, its
+// row and segment (kept up to date incrementally: no division per unit).
+struct UPos {
+  int64_t v, row, seg;
+};
+
+template <int DT, int GRAN, int OUT>
+struct Walk {
+  static constexpr int kB = Raw<DT>::kBytes;
+  static constexpr int kUnitBlocks = unit_blocks(OUT, DT);
+  const TensorRef& T;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t nbk, nblk, spr;
+  __device__ Walk(const TensorRef& t, uint8_t* c, uint8_t* s) : T(t), codes(c), scales(s) {
+    nbk = T.K >> 4;
+    nblk = T.M * nbk;
+    spr = (nbk + kUnitBlocks - 1) / kUnitBlocks;
+  }
+  __device__ UPos at(int64_t v) const {
+    if (GRAN == kGranTensor) return UPos{v, 0, 0};
+    const int64_t row = v / spr;
+    return UPos{v, row, v - row * spr};
+  }
+  __device__ UPos next(UPos p) const {
+    p.v += 1;
+    if (GRAN != kGranTensor) {
+      p.seg += 1;
+      if (p.seg == spr) { p.seg = 0; p.row += 1; }
+    }
+    return p;
+  }
+  // resources for the unit at p (valid: the unit exists; rows_read: rows of
+  // the tensor that hold data, later rows read as zeros)
+  __device__ Unit unit(const UPos& p, bool valid, int64_t rows_read) const {
+    int64_t b0, nvalid;
+    if (GRAN == kGranTensor) {
+      b0 = p.v * kUnitBlocks;
+      nvalid = min((int64_t)kUnitBlocks, nblk - b0);
+    } else {
+      b0 = p.row * nbk + p.seg * kUnitBlocks;
+      nvalid = min((int64_t)kUnitBlocks, nbk - p.seg * kUnitBlocks);
+    }
+    if (!valid) nvalid = 0;
+    const int64_t nread = (GRAN == kGranGroup && p.row >= rows_read) ? 0 : nvalid;
+    Unit u;
+    u.x = make_rsrc(static_cast<const char*>(T.x) + b0 * kB, nread * kB);
+    if (OUT == kOutQuant) {
+      u.out = make_rsrc(codes + b0 * 8, nvalid * 8);
+      u.scl = make_rsrc(scales + b0, nvalid);
+    } else {
+      u.out = make_rsrc(static_cast<char*>(T.y) + b0 * kB, nvalid * kB);
+      u.scl = u.out;
+    }
+    return u;
+  }
+};
+
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
+  __shared__ float lds[4][256];
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  constexpr bool kXhat = OUT == kOutQdq;
+  constexpr int kB = Raw<DT>::kBytes;
+  constexpr int kNB = unit_blocks(OUT, DT) / 64;
+
+  if (OUT == kOutQuant) side_outputs<GRAN>(args);
+
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t total = args.total_units;
   const int64_t per = (total + nwaves - 1) / nwaves;
   int64_t u = wave * per;
   const int64_t u_end = min(total, u + per);
   if (u >= u_end) return;
 
-  // locate the tensor holding unit u
   int ti = 0;
   while (ti + 1 < args.n && args.t[ti + 1].unit_begin <= u) ti++;
-
   const float six_b = args.six_b;
+  const uint32_t off_x = lane * kB, off_c = lane * 8, off_s = lane;
+
   for (;;) {
     const TensorRef T = args.t[ti];
-    const int64_t nbk = T.K >> 4;
-    const int64_t unit_end_t = (ti + 1 < args.n) ? args.t[ti + 1].unit_begin : total;
-    const int64_t dr = 64 / nbk, dc = 64 % nbk;
-    Pos p = pos_of((u - T.unit_begin) * 64 + lane, nbk);
-    const int64_t M_rows = T.M;            // rows to write
-    // rows holding data: all of them, or for a grouped launch the rows
-    // before offs[G-1] (clamped to the allocation)
-    int64_t M_read = T.M;
-    if (GRAN == kGranGroup) M_read = min(max((int64_t)args.offs[args.G - 1], (int64_t)0), T.M);
+    const Walk<DT, GRAN, OUT> W(T, args.codes, args.scales);
+    const int64_t stop = min(u_end, (ti + 1 < args.n) ? args.t[ti + 1].unit_begin : total);
+    int64_t rows_read = T.M;  // grouped: rows before offs[G-1] hold data
+    if (GRAN == kGranGroup) rows_read = min(max((int64_t)ld_const(args.offs, args.G - 1), (int64_t)0), T.M);
 
     float S_enc = 1.0f, S_dec = 1.0f;
-    int64_t cur_row = -1;
     if (GRAN == kGranTensor) {
-      S_enc = global_encode_scale(T.amax[0], six_b);
+      S_enc = global_encode_scale(ld_const(T.amax, 0), six_b);
       S_dec = 1.0f / S_enc;
+      tab.build(S_enc, S_dec, lane);
     }
-    const int64_t stop = min(u_end, unit_end_t);
-    for (; u < stop; ++u, advance(p, nbk, dr, dc)) {
-      if (p.row >= M_rows) continue;
-      const int64_t elem = p.row * T.K + p.cb * 16;
-      if (GRAN == kGranGroup && p.row >= M_read) {
-        // over-allocated tail: not read, zero codes and scale
-        store_codes(args.codes, elem >> 1, 0u, 0u);
-        args.scales[p.row * nbk + p.cb] = 0;
-        continue;
+    int64_t tab_row = -1;
+
+    // one unit: quantize the lane's block held in `raw`, store its outputs
+    // (two stores). Units past the range compute on zeros and their stores
+    // fall outside their resources.
+    auto process = [&](const Raw<DT>* raw, const UPos& pos, bool valid, const Unit& U) {
+      if (GRAN != kGranTensor) {
+        const int64_t row = pos.row;  // wave-uniform
+        if (valid && row != tab_row) {
+          const float A = (GRAN == kGranRow) ? ld_const(T.amax, row)
+                                             : ld_const(args.group_amax, group_of(args.offs, args.G, row));
+          S_enc = global_encode_scale(A, six_b);
+          S_dec = 1.0f / S_enc;
+          tab.build(S_enc, S_dec, lane);
+          tab_row = row;
+        }
       }
-      if (GRAN != kGranTensor && p.row != cur_row) {
-        float A;
-        if (GRAN == kGranRow) A = T.amax[p.row];
-        else A = args.group_amax[group_of(args.offs, args.G, p.row)];
-        S_enc = global_encode_scale(A, six_b);
-        S_dec = 1.0f / S_enc;
-        cur_row = p.row;
+#pragma unroll
+      for (int j = 0; j < kNB; j++) {
+        float x[16], xh[16];
+        raw[j].unpack(x);
+        BlockOut o;
+        quantize_block<RECIPE, METRIC, PREC, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
+        if (OUT == kOutQuant) {
+          store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
+          store_scale(U.scl, off_s + j * 64, o.scale);
+        } else {
+          store16<DT>(U.out, off_x + j * 64 * kB, xh);
+        }
       }
-      float x[16];
-      Io<DT>::load16(T.x, elem, x);
-      BlockOut o;
-      float xh[16];
-      constexpr bool kXhat = OUT == kOutQdq;
-      if (!block_1x16<RECIPE, METRIC, PREC, false, kXhat>(x, S_enc, S_dec, o, xh))
-        block_1x16<RECIPE, METRIC, PREC, true, kXhat>(x, S_enc, S_dec, o, xh);
-      if (OUT == kOutQuant) {
-        store_codes(args.codes, elem >> 1, o.c0, o.c1);
-        args.scales[p.row * nbk + p.cb] = (uint8_t)o.scale;
-      } else {
-        Io<DT>::store16(T.y, elem, xh);
-      }
+    };
+
+    auto load_unit = [&](Raw<DT>* r, const Unit& U) {
+#pragma unroll
+      for (int j = 0; j < kNB; j++) r[j].load(U.x, off_x + j * 64 * kB);
+    };
+
+    // Two units in flight, A and B: each is reloaded right after its stores,
+    // so between a load and its use the same memory operations issue on
+    // every path (the two dummy stores below stand in for the stores of a
+    // unit before the first), and the compiler's wait counts only the loads
+    // issued since.
+    const int64_t v_stop = stop - T.unit_begin;
+    UPos pa = W.at(u - T.unit_begin);
+    UPos pb = W.next(pa);
+    Unit UA = W.unit(pa, true, rows_read);
+    Unit UB = W.unit(pb, pb.v < v_stop, rows_read);
+    Raw<DT> A[kNB], B[kNB];
+    load_unit(A, UA);
+    dummy_stores<kNB>();
+    load_unit(B, UB);
+    for (; pa.v < v_stop;) {
+      process(A, pa, true, UA);
+      pa = W.next(pb);
+      UA = W.unit(pa, pa.v < v_stop, rows_read);
+      load_unit(A, UA);
+      process(B, pb, pb.v < v_stop, UB);
+      pb = W.next(pa);
+      UB = W.unit(pb, pb.v < v_stop, rows_read);
+      load_unit(B, UB);
     }
+    u = stop;
     if (u >= u_end) break;
     ti++;
   }
@@ -358,59 +587,141 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
 // ------------------------------------------------------------ 16x16 kernel
 
 // A unit is one 16-row band times four consecutive tiles: lane = 16 * tile +
-// row in tile, so a wave reads 16 rows x 64 columns.
+// row in tile, so a wave reads 16 rows x 64 columns. Lanes of a ragged last
+// group of tiles idle with out-of-range offsets.
 template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
+  __shared__ float lds[4][256];
+  constexpr int kB = Raw<DT>::kBytes;
+  constexpr int kEB = kB / 16;  // bytes per element
+  constexpr bool kXhat = OUT == kOutQdq;
   const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
   const int r16 = lane & 15, tq = lane >> 4;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t nbk = args.K >> 4;
-  const int64_t groups_per_band = (nbk + 3) >> 2;
-  const int64_t total = (args.M >> 4) * groups_per_band;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t K = args.K, nbk = K >> 4;
+  const int64_t gpb = (nbk + 3) >> 2;  // groups of four tiles per band
+  const int64_t total = (args.M >> 4) * gpb;
   const int64_t per = (total + nwaves - 1) / nwaves;
   int64_t u = wave * per;
   const int64_t u_end = min(total, u + per);
   const float six_b = args.six_b;
 
+  if (OUT == kOutQuant && args.sdec_out) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gsz = (int64_t)gridDim.x * blockDim.x;
+    if (GRAN == kGranTensor) {
+      if (gid == 0) args.sdec_out[0] = 1.0f / global_encode_scale(args.amax[0], six_b);
+    } else {
+      for (int64_t r = gid; r < args.M; r += gsz) args.sdec_out[r] = 1.0f / global_encode_scale(args.amax[r], six_b);
+    }
+  }
+  if (u >= u_end) return;
+
   float S_enc = 1.0f, S_dec = 1.0f;
   if (GRAN == kGranTensor) {
-    S_enc = global_encode_scale(args.amax[0], six_b);
+    S_enc = global_encode_scale(ld_const(args.amax, 0), six_b);
     S_dec = 1.0f / S_enc;
+    tab.build(S_enc, S_dec, lane);
   }
   int64_t cur_band = -1;
-  for (; u < u_end; ++u) {
-    const int64_t band = u / groups_per_band;
-    const int64_t cb = (u % groups_per_band) * 4 + tq;
-    const int64_t row = band * 16 + r16;
-    if (GRAN == kGranRow && band != cur_band) {
-      // tile-uniform contract: the tile uses its first row's amax
-      const float A_mine = args.amax[row];
-      const float A = __shfl(A_mine, 0, 16);
-      if (__float_as_uint(A_mine) != __float_as_uint(A) && args.status) atomicOr(args.status, kStatusTileNonuniform);
+  const int64_t x_bytes = args.M * K * kEB;
+  const int64_t c_bytes = args.M * K / 2;
+  const int64_t s_bytes = args.M * nbk;
+
+  struct U16 {
+    Rsrc x, out, scl;
+    uint32_t ox, oo, os;  // lane offsets
+  };
+  auto unit = [&](int64_t uu, bool valid) {
+    const int64_t band = uu / gpb, tg = uu - band * gpb;
+    const bool active = valid && (tg * 4 + tq < nbk);
+    const int64_t ex = band * 16 * K + tg * 64;  // first element of the unit
+    U16 r;
+    r.x = make_rsrc(static_cast<const char*>(args.x) + ex * kEB, valid ? x_bytes - ex * kEB : 0);
+    r.ox = active ? (uint32_t)((r16 * K + tq * 16) * kEB) : kOOB;
+    if (OUT == kOutQuant) {
+      r.out = make_rsrc(args.codes + ex / 2, valid ? c_bytes - ex / 2 : 0);
+      r.oo = active ? (uint32_t)(r16 * (K / 2) + tq * 8) : kOOB;
+      const int64_t es = band * 16 * nbk + tg * 4;
+      r.scl = make_rsrc(args.scales + es, valid ? s_bytes - es : 0);
+      r.os = active ? (uint32_t)(r16 * nbk + tq) : kOOB;
+    } else {
+      r.out = make_rsrc(static_cast<char*>(args.y) + ex * kEB, valid ? x_bytes - ex * kEB : 0);
+      r.oo = r.ox;
+      r.scl = r.out;
+      r.os = kOOB;
+    }
+    return r;
+  };
+
+  auto process = [&](const Raw<DT>& raw, int64_t uu, bool valid, const U16& U) {
+    const int64_t band = uu / gpb;
+    if (GRAN == kGranRow && valid && band != cur_band) {
+      // tile-uniform contract: the band uses its first row's amax, and a band
+      // whose rows differ is flagged
+      const float A = ld_const(args.amax, band * 16);
+      bool uniform = true;
+#pragma unroll
+      for (int i = 1; i < 16; i++) uniform &= __float_as_uint(ld_const(args.amax, band * 16 + i)) == __float_as_uint(A);
+      if (!uniform && args.status && lane == 0) atomicOr(args.status, kStatusTileNonuniform);
       S_enc = global_encode_scale(A, six_b);
       S_dec = 1.0f / S_enc;
+      tab.build(S_enc, S_dec, lane);
       cur_band = band;
     }
-    if (cb >= nbk) continue;  // whole 16-lane group idles together
-    const int64_t elem = row * args.K + cb * 16;
-    float x[16];
-    Io<DT>::load16(args.x, elem, x);
+    float x[16], xh[16];
+    raw.unpack(x);
     BlockOut o;
-    float xh[16];
-    constexpr bool kXhat = OUT == kOutQdq;
-    if (!tile_16x16<RECIPE, METRIC, PREC, false, kXhat>(x, S_enc, S_dec, o, xh))
-      tile_16x16<RECIPE, METRIC, PREC, true, kXhat>(x, S_enc, S_dec, o, xh);
+    if (!tile_16x16<RECIPE, METRIC, PREC, false, kXhat, true>(x, S_enc, S_dec, tab, o, xh))
+      tile_16x16<RECIPE, METRIC, PREC, true, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
     if (OUT == kOutQuant) {
-      store_codes(args.codes, elem >> 1, o.c0, o.c1);
-      args.scales[row * nbk + cb] = (uint8_t)o.scale;
+      store_codes(U.out, U.oo, o.c0, o.c1);
+      store_scale(U.scl, U.os, o.scale);
     } else {
-      Io<DT>::store16(args.y, elem, xh);
+      store16<DT>(U.out, U.oo, xh);
     }
+  };
+
+  // two units in flight, as in the 1x16 kernel
+  U16 UA = unit(u, true), UB = unit(u + 1, u + 1 < u_end);
+  Raw<DT> A, B;
+  A.load(UA.x, UA.ox);
+  dummy_stores<1>();
+  B.load(UB.x, UB.ox);
+  for (; u < u_end; u += 2) {
+    const bool hasB = u + 1 < u_end;
+    process(A, u, true, UA);
+    UA = unit(u + 2, u + 2 < u_end);
+    A.load(UA.x, UA.ox);
+    process(B, u + 1, hasB, UB);
+    UB = unit(u + 3, u + 3 < u_end);
+    B.load(UB.x, UB.ox);
   }
 }
 
 // ------------------------------------------------------------ dequantize
+
+// Plain global stores of 16 decoded values as the output type.
+template <int DT> __device__ __forceinline__ void put16(void* base, int64_t idx, const float* y);
+template <> __device__ __forceinline__ void put16<kBF16>(void* base, int64_t idx, const float* y) {
+  uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx);
+  p[0] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+  p[1] = make_uint4(pack_bf16(y[8], y[9]), pack_bf16(y[10], y[11]), pack_bf16(y[12], y[13]), pack_bf16(y[14], y[15]));
+}
+template <> __device__ __forceinline__ void put16<kFP16>(void* base, int64_t idx, const float* y) {
+  uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx);
+  p[0] = make_uint4(pack_f16(y[0], y[1]), pack_f16(y[2], y[3]), pack_f16(y[4], y[5]), pack_f16(y[6], y[7]));
+  p[1] = make_uint4(pack_f16(y[8], y[9]), pack_f16(y[10], y[11]), pack_f16(y[12], y[13]), pack_f16(y[14], y[15]));
+}
+template <> __device__ __forceinline__ void put16<kFP32>(void* base, int64_t idx, const float* y) {
+  float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
+#pragma unroll
+  for (int i = 0; i < 4; i++) p[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+}
+
 
 template <int DT, int GRAN>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -425,16 +736,36 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
     const float D = e4m3_value(scales[b]) * S_dec;
     float xh[16];
     decode16(c.x, c.y, D, xh);
-    Io<DT>::store16(y, b * 16, xh);
+    put16<DT>(y, b * 16, xh);
   }
 }
 
 // ------------------------------------------------------------ amax
 
+// NaN-dropping magnitude max over packed 16-bit pairs: with m = |h| bits,
+// adding `bias` (0x7F for bf16, 0x3FF for f16) sends exactly the NaN patterns
+// past 0x7FFF, where a signed 16-bit max ignores them.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ s16x2 pair_key(uint32_t w) {
+  const uint32_t bias = (DT == kBF16) ? 0x007F007Fu : 0x03FF03FFu;
+  return __builtin_bit_cast(s16x2, w & 0x7FFF7FFFu) + __builtin_bit_cast(s16x2, bias);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pair_key_to_f32_bits(s16x2 k) {
+  const int bias = (DT == kBF16) ? 0x7F : 0x3FF;
+  const int m = max((int)k.x, (int)k.y) - bias;  // magnitude bits of the max
+  if (DT == kBF16) return (uint32_t)m << 16;
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)m);
+  return __float_as_uint((float)h);
+}
+
 // NaN-dropping |x| max as unsigned bits (NaN patterns count as +0); the
 // order of non-negative binary32 values equals the order of their bits.
 __device__ __forceinline__ uint32_t mag_bits(float v) {
-  uint32_t m = __float_as_uint(v) & 0x7FFFFFFFu;
+  const uint32_t m = __float_as_uint(v) & 0x7FFFFFFFu;
   return m <= 0x7F800000u ? m : 0u;
 }
 
@@ -444,27 +775,69 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// max |x| (as binary32 bits) over 16-element blocks b, b + stride, ... < n16
+// of x; four blocks in flight per lane.
+template <int DT>
+__device__ __forceinline__ uint32_t absmax_blocks(const void* x, int64_t b, int64_t n16, int64_t stride) {
+  if constexpr (DT == kFP32) {
+    const float4* p = static_cast<const float4*>(x);
+    uint32_t m = 0;
+    for (; b < n16; b += stride) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float4 v = p[b * 4 + i];
+        m = max(max(m, mag_bits(v.x)), max(mag_bits(v.y), max(mag_bits(v.z), mag_bits(v.w))));
+      }
+    }
+    return m;
+  } else {
+    const uint4* p = static_cast<const uint4*>(x);
+    s16x2 k = pair_key<DT>(0u);
+    for (; b + 3 * stride < n16; b += 4 * stride) {
+      uint4 r[8];
+#pragma unroll
+      for (int j = 0; j < 4; j++) { r[2 * j] = p[(b + j * stride) * 2]; r[2 * j + 1] = p[(b + j * stride) * 2 + 1]; }
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        k = __builtin_elementwise_max(k, pair_key<DT>(r[j].x));
+        k = __builtin_elementwise_max(k, pair_key<DT>(r[j].y));
+        k = __builtin_elementwise_max(k, pair_key<DT>(r[j].z));
+        k = __builtin_elementwise_max(k, pair_key<DT>(r[j].w));
+      }
+    }
+    for (; b < n16; b += stride) {
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const uint4 r = p[b * 2 + j];
+        k = __builtin_elementwise_max(k, pair_key<DT>(r.x));
+        k = __builtin_elementwise_max(k, pair_key<DT>(r.y));
+        k = __builtin_elementwise_max(k, pair_key<DT>(r.z));
+        k = __builtin_elementwise_max(k, pair_key<DT>(r.w));
+      }
+    }
+    return pair_key_to_f32_bits<DT>(k);
+  }
+}
+
 __global__ void k_zero_u32(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// Per-tensor amax: many small workgroups, so that their completions (and
+// their one atomic each) spread over the launch; a workgroup whose maximum
+// does not exceed the value already stored skips its atomic. Same-address
+// atomics serialize at the memory side, so they are kept few.
 template <int DT>
 __global__ void __launch_bounds__(256) k_amax_tensor(const void* x, int64_t n16, uint32_t* out) {
-  uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n16; b += stride) {
-    float v[16];
-    Io<DT>::load16(x, b * 16, v);
-#pragma unroll
-    for (int i = 0; i < 16; i++) m = max(m, mag_bits(v[i]));
-  }
+  uint32_t m = absmax_blocks<DT>(x, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, n16, stride);
   m = wave_max_u32(m);
   __shared__ uint32_t part[4];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t r = max(max(part[0], part[1]), max(part[2], part[3]));
-    atomicMax(out, r);
+    const uint32_t r = max(max(part[0], part[1]), max(part[2], part[3]));
+    if (r > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(out, r);
   }
 }
 
@@ -475,13 +848,7 @@ __global__ void __launch_bounds__(256) k_amax_row(const void* x, int64_t M, int6
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   const int64_t nbk = K >> 4;
   for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < M; r += nwaves) {
-    uint32_t m = 0;
-    for (int64_t cb = lane; cb < nbk; cb += 64) {
-      float v[16];
-      Io<DT>::load16(x, r * K + cb * 16, v);
-#pragma unroll
-      for (int i = 0; i < 16; i++) m = max(m, mag_bits(v[i]));
-    }
+    uint32_t m = absmax_blocks<DT>(static_cast<const char*>(x) + r * K * (DT == kFP32 ? 4 : 2), lane, nbk, 64);
     m = wave_max_u32(m);
     if (lane == 0) out[r] = __uint_as_float(m);
   }
@@ -495,78 +862,76 @@ __global__ void k_band16(float* out, int64_t nbands) {
   }
 }
 
-// S_dec outputs: per tensor [1], per row [M] or per group [G]
-__global__ void k_sdec(const float* amax, int64_t n, float six_b, float* out) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    out[i] = 1.0f / global_encode_scale(amax[i], six_b);
-}
-
-// offs contract check: monotone, multiples of 16, last <= M_alloc
-__global__ void k_check_offs(const int32_t* offs, int G, int64_t M_alloc, int32_t* status) {
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    const int32_t prev = g ? offs[g - 1] : 0;
-    const bool bad = offs[g] < prev || (offs[g] & 15) || (g == G - 1 && (int64_t)offs[g] > M_alloc);
-    if (bad && status) atomicOr(status, kStatusBadOffs);
-  }
-}
-
 // ------------------------------------------------------------ dispatch
 
 // workgroups of 256 threads for an n-item elementwise helper (capped)
 static unsigned small_grid(int64_t n) {
-  int64_t g = (n + 255) / 256;
+  const int64_t g = (n + 255) / 256;
   return (unsigned)(g < 1 ? 1 : (g > 1024 ? 1024 : g));
 }
 
-template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
-static hipError_t launch_1x16_t(const Args1x16<1>& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_1x16<1, DT, RECIPE, METRIC, PREC, GRAN, OUT>), dim3(grid), dim3(256), 0, s, a);
+// Workgroups of 256 threads resident at once for kernel fn: the grid of the
+// unit-walking kernels (each wave then walks a contiguous unit range).
+static int64_t resident_grid(const void* fn) {
+  int dev = 0, cus = 0, per_cu = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu <= 0) per_cu = 2;
+  return (int64_t)cus * per_cu;
+}
+
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
+static hipError_t launch_1x16_t(const Args1x16<NT>& a, hipStream_t s) {
+  auto* fn = &k_1x16<NT, DT, RECIPE, METRIC, PREC, GRAN, OUT>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
-static hipError_t launch_list_t(const Args1x16<kMaxList>& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_1x16<kMaxList, DT, RECIPE, METRIC, PREC, GRAN, OUT>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
-static hipError_t launch_16x16_t(const Args16x16& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_16x16<DT, RECIPE, METRIC, PREC, GRAN, OUT>), dim3(grid), dim3(256), 0, s, a);
+static hipError_t launch_16x16_t(const Args16x16& a, hipStream_t s) {
+  auto* fn = &k_16x16<DT, RECIPE, METRIC, PREC, GRAN, OUT>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t units = (a.M / 16) * ((a.K / 16 + 3) / 4);
+  const int64_t grid = max((int64_t)1, min(resident, (units + 3) / 4));
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // Expand the runtime knobs into template instances. Every mode is a compiled
 // specialization; the kernels never branch on a mode.
-#define FOS_MODES(DT, GRAN, OUT, FN)                                                         \
-  if (recipe == kNVFP4) return FN<DT, kNVFP4, kMSE, kErrExact, GRAN, OUT>(a, grid, s);      \
-  if (metric == kMAE && prec == kErrExact) return FN<DT, k4over6, kMAE, kErrExact, GRAN, OUT>(a, grid, s); \
-  if (metric == kMAE && prec == kErrFP16) return FN<DT, k4over6, kMAE, kErrFP16, GRAN, OUT>(a, grid, s);   \
-  if (metric == kMSE && prec == kErrExact) return FN<DT, k4over6, kMSE, kErrExact, GRAN, OUT>(a, grid, s); \
-  return FN<DT, k4over6, kMSE, kErrFP16, GRAN, OUT>(a, grid, s);
+#define FOS_MODES(DT, GRAN, OUT, CALL)                                                          \
+  if (recipe == kNVFP4) return CALL(DT, kNVFP4, kMSE, kErrExact, GRAN, OUT);                     \
+  if (metric == kMAE && prec == kErrExact) return CALL(DT, k4over6, kMAE, kErrExact, GRAN, OUT); \
+  if (metric == kMAE && prec == kErrFP16) return CALL(DT, k4over6, kMAE, kErrFP16, GRAN, OUT);   \
+  if (metric == kMSE && prec == kErrExact) return CALL(DT, k4over6, kMSE, kErrExact, GRAN, OUT); \
+  return CALL(DT, k4over6, kMSE, kErrFP16, GRAN, OUT);
 
-#define FOS_DTYPES(GRAN, OUT, FN)                       \
-  if (dt == kBF16) { FOS_MODES(kBF16, GRAN, OUT, FN) } \
-  if (dt == kFP16) { FOS_MODES(kFP16, GRAN, OUT, FN) } \
-  { FOS_MODES(kFP32, GRAN, OUT, FN) }
+#define FOS_DTYPES(GRAN, OUT, CALL)                       \
+  if (dt == kBF16) { FOS_MODES(kBF16, GRAN, OUT, CALL) } \
+  if (dt == kFP16) { FOS_MODES(kFP16, GRAN, OUT, CALL) } \
+  { FOS_MODES(kFP32, GRAN, OUT, CALL) }
 
-hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a, int grid,
+#define CALL_Q1(DT, R, M, P, G, O) launch_1x16_t<1, DT, R, M, P, G, O>(a, s)
+#define CALL_QL(DT, R, M, P, G, O) launch_1x16_t<kMaxList, DT, R, M, P, G, O>(a, s)
+#define CALL_T(DT, R, M, P, G, O) launch_16x16_t<DT, R, M, P, G, O>(a, s)
+
+hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a,
                              hipStream_t s) {
-  if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, launch_1x16_t) }
-  if (gran == kGranRow) { FOS_DTYPES(kGranRow, kOutQuant, launch_1x16_t) }
-  FOS_DTYPES(kGranGroup, kOutQuant, launch_1x16_t)
+  if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, CALL_Q1) }
+  if (gran == kGranRow) { FOS_DTYPES(kGranRow, kOutQuant, CALL_Q1) }
+  FOS_DTYPES(kGranGroup, kOutQuant, CALL_Q1)
 }
 
-hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, int grid,
-                           hipStream_t s) {
-  if (dt == kBF16) { FOS_MODES(kBF16, kGranTensor, kOutQdq, launch_list_t) }
-  FOS_MODES(kFP16, kGranTensor, kOutQdq, launch_list_t)
+hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, hipStream_t s) {
+  if (dt == kBF16) { FOS_MODES(kBF16, kGranTensor, kOutQdq, CALL_QL) }
+  FOS_MODES(kFP16, kGranTensor, kOutQdq, CALL_QL)
 }
 
-hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, int grid,
-                              hipStream_t s) {
-  if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, launch_16x16_t) }
-  FOS_DTYPES(kGranRow, kOutQuant, launch_16x16_t)
+hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, hipStream_t s) {
+  if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, CALL_T) }
+  FOS_DTYPES(kGranRow, kOutQuant, CALL_T)
 }
 
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,
@@ -599,19 +964,8 @@ hipError_t launch_amax(int dt, int gran, const void* x, int64_t M, int64_t K, fl
   return hipGetLastError();
 }
 
-hipError_t launch_sdec(const float* amax, int64_t n, float six_b, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_sdec, dim3(small_grid(n)), dim3(256), 0, s, amax, n, six_b, out);
-  return hipGetLastError();
-}
-
 hipError_t launch_zero_u32(void* p, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero_u32, dim3(small_grid(n)), dim3(256), 0, s,
-                     static_cast<uint32_t*>(p), n);
-  return hipGetLastError();
-}
-
-hipError_t launch_check_offs(const int32_t* offs, int G, int64_t M_alloc, int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_check_offs, dim3(1), dim3(256), 0, s, offs, G, M_alloc, status);
+  hipLaunchKernelGGL(k_zero_u32, dim3(small_grid(n)), dim3(256), 0, s, static_cast<uint32_t*>(p), n);
   return hipGetLastError();
 }
 
