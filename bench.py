@@ -45,6 +45,28 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+KERNEL_TRACE = os.path.join(ROOT, "profiles", "kernel_trace_bench_workloads.txt")
+
+
+def read_profile_value(path, key):
+    """A `key = value` figure from a committed profile summary, or None when the
+    file is missing or was taken on other kernel code."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.split("#", 1)[0] if not line.lstrip().startswith("#") else line.lstrip("# ")
+        if "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv[key])
+    except (KeyError, ValueError):
+        return None
+
+
 def read_counters():
     """HBM bytes per quantize launch from the committed rocprofv3 counter
     summary, or None when it is missing or was taken on other kernel code."""
@@ -103,7 +125,12 @@ def main():
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3: a few quantize launches and a known-size copy, no JSON")
+    ap.add_argument("--write-profiles", metavar="DIR",
+                    help="summarize rocprofv3 CSV output under DIR (kt/, fetch/, write/, sq/) into profiles/")
     args = ap.parse_args()
+    if args.write_profiles:
+        write_profiles(args.write_profiles)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
@@ -151,30 +178,28 @@ def main():
         return
 
     # ---------------------------------------------------------------- main step
-    def step(i, evs=None):
-        if evs is not None:
-            evs[0].record()
+    def step(i, ev_q=None):
         fos.fos_amax(xs[i], "tensor", out=amax[i])
-        if evs is not None:
-            evs[1].record()
+        if ev_q is not None:
+            ev_q.record()
         fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)
-        if evs is not None:
-            evs[2].record()
 
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
     for i in range(args.warmup):
         step(i % nset)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    # events: marks[i] opens step i (and closes step i-1's quantize), qs[i]
+    # separates step i's amax from its quantize
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    qs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
-        step((args.warmup + i) % nset, evs[i])
-    end.record()
+        marks[i].record()
+        step((args.warmup + i) % nset, qs[i])
+    marks[-1].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    a_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    q_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    total_ms = marks[0].elapsed_time(marks[-1])
+    a_ms = [marks[i].elapsed_time(qs[i]) for i in range(args.steps)]
+    q_ms = [qs[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     ms_per_step = total_ms / args.steps
     q_avg_ms = float(np.mean(q_ms))
     a_avg_ms = float(np.mean(a_ms))
@@ -228,6 +253,7 @@ def main():
         other = other_workloads(fos, synthdata, torch, np)
 
     traffic = read_counters()
+    rocprof_us = read_profile_value(KERNEL_TRACE, "quantize_kernel_avg_us")
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -249,7 +275,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "fos_quantize (k_1x16, bf16, 4over6 MSE exact)",
                      "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(q_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": q_bytes, "avg_launch_us": round(q_avg_ms * 1e3, 2)},
+                     "algorithmic_bytes_per_launch": q_bytes, "avg_launch_us": round(q_avg_ms * 1e3, 2),
+                     "rocprof_kernel_avg_us": rocprof_us},
         "amax_kernel": {"avg_launch_us": round(a_avg_ms * 1e3, 2),
                         "achieved_GBs": round(in_bytes / (a_avg_ms * 1e-3) / 1e9, 1)},
         "bit_exact_sample": bit_exact,
@@ -257,6 +284,147 @@ def main():
         "other_workloads": other,
     }
     print(json.dumps(result), flush=True)
+
+
+# ---------------------------------------------------------------- profile summaries
+
+QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0>(fos::Args1x16<1>)"
+COPY_BYTES = 256 << 20     # the profile pass's calibration copy
+PROFILE_CMDS = {
+    "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o kt -- "
+          "python3 $REPO/bench.py --steps 200 --warmup 20 --no-cpu-baseline",
+    "fetch": "timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o fetch -- "
+             "python3 $REPO/bench.py --profile-pass",
+    "write": "timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o write -- "
+             "python3 $REPO/bench.py --profile-pass",
+    "sq": "timeout -s KILL 90 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES "
+          "SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VALU_CVT GRBM_GUI_ACTIVE --output-format csv "
+          "-d $OUT/sq -o sq -- python3 $REPO/bench.py --profile-pass",
+}
+_DT = {"0": "bf16", "1": "fp16", "2": "fp32"}
+_RC = {"0": "nvfp4", "1": "4over6"}
+_MT = {"0": "mae", "1": "mse"}
+_PR = {"0": "exact", "1": "fp16err"}
+_GR = {"0": "tensor", "1": "row", "2": "grouped"}
+_OUT = {"0": "quantize", "1": "qdq"}
+
+
+def describe_kernel(name: str) -> str:
+    """Readable mode of one of this library's kernel template instances."""
+    import re
+    m = re.match(r"void fos::k_1x16<(\d+), (\d), (\d), (\d), (\d), (\d), (\d)>", name)
+    if m:
+        nt, dt, rc, mt, pr, gr, out = m.groups()
+        lst = f" list<{nt}>" if nt != "1" else ""
+        err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
+        return f"1x16 {_OUT[out]}{lst} {_DT[dt]} {_RC[rc]}{err} {_GR[gr]}"
+    m = re.match(r"void fos::k_16x16<(\d), (\d), (\d), (\d), (\d), (\d)>", name)
+    if m:
+        dt, rc, mt, pr, gr, out = m.groups()
+        err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
+        return f"16x16 {_OUT[out]} {_DT[dt]} {_RC[rc]}{err} {_GR[gr]}"
+    if "k_amax_tensor" in name:
+        return "amax per tensor (" + {"0": "bf16", "1": "fp16", "2": "fp32"}.get(name.split("<")[1][0], "?") + ")"
+    if "k_zero_u32" in name:
+        return "clear the amax word"
+    if "copyBuffer" in name:
+        return "runtime copy (buffer set clones)"
+    return ""
+
+
+def _counters(path):
+    """{(kernel, counter): [per-dispatch values in dispatch order]} from a rocprofv3 counter CSV."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], r["Counter_Name"])
+        per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+        per[key][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: [v[d] for d in sorted(v)] for k, v in per.items()}
+
+
+def write_profiles(d):
+    """Write profiles/kernel_trace_bench_workloads.txt and the quantize kernel's
+    counter summary from the CSV files rocprofv3 wrote under d."""
+    import csv
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    ksha = kernel_source_hash()
+
+    # kernel trace summary (rocprofv3 --stats)
+    stats = list(csv.DictReader(open(os.path.join(d, "kt", "kt_kernel_stats.csv"))))
+    lines = ["# rocprofv3 --kernel-trace --stats summary of the default bench (all workloads)",
+             "# command (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):",
+             "#   " + PROFILE_CMDS["kt"],
+             f"# kernel_source_sha256_16 = {ksha}",
+             "# durations in microseconds, per dispatch",
+             f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>6}  mode / kernel"]
+    q_avg = None
+    for r in stats:
+        name = r["Name"]
+        if name == QUANT_KERNEL:
+            q_avg = float(r["AverageNs"]) / 1e3
+        desc = describe_kernel(name)
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):5.1f}%  "
+                     f"{desc + ' | ' if desc else ''}{name[:110]}")
+    if q_avg is not None:
+        lines.append(f"quantize_kernel_avg_us = {q_avg:.2f}   # {describe_kernel(QUANT_KERNEL)}, the bench step's kernel")
+    open(os.path.join(out_dir, "kernel_trace_bench_workloads.txt"), "w").write("\n".join(lines) + "\n")
+
+    # HBM counters of the quantize kernel, calibrated on a copy of known size
+    f = _counters(os.path.join(d, "fetch", "fetch_counter_collection.csv"))
+    w = _counters(os.path.join(d, "write", "write_counter_collection.csv"))
+    copy_name = "__amd_rocclr_copyBuffer"
+    cf = f[(copy_name, "FETCH_SIZE")][-4:]   # the profile pass ends with four 256 MiB copies
+    cw = w[(copy_name, "WRITE_SIZE")][-4:]
+    qf = f[(QUANT_KERNEL, "FETCH_SIZE")]
+    qw = w[(QUANT_KERNEL, "WRITE_SIZE")]
+    mean = lambda v: sum(v) / len(v)
+    fetch_factor = COPY_BYTES / (mean(cf) * 1024)
+    write_factor = COPY_BYTES / (mean(cw) * 1024)
+    rd = mean(qf) * 1024 * fetch_factor
+    wr = mean(qw) * 1024 * write_factor
+    n = 8192 * 4096
+    alg = n * 2 + n // 2 + n // 16
+    lines = ["# rocprofv3 counter summary: fos_quantize, 1x16 blocks, bf16 8192x4096 N(0,1), four-over-six MSE exact,",
+             "# E4M3 bound 448, per-tensor scale (the bench step's quantize kernel)",
+             "# commands (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):",
+             "#   " + PROFILE_CMDS["fetch"], "#   " + PROFILE_CMDS["write"], "#   " + PROFILE_CMDS["sq"],
+             f"#   python3 $REPO/bench.py --write-profiles $OUT",
+             "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch. The factors scale them to bytes so that the",
+             f"# profile pass's plain copy of {COPY_BYTES} bytes reads and writes exactly that many bytes.",
+             f"kernel = {QUANT_KERNEL}",
+             f"kernel_source_sha256_16 = {ksha}",
+             f"dispatches = {len(qf)}",
+             f"fetch_size_kib = {mean(qf):.1f}",
+             f"write_size_kib = {mean(qw):.1f}",
+             f"copy_fetch_size_kib = {mean(cf):.1f}",
+             f"copy_write_size_kib = {mean(cw):.1f}",
+             f"fetch_factor = {fetch_factor:.4f}",
+             f"write_factor = {write_factor:.4f}",
+             f"hbm_read_bytes_per_launch = {rd:.0f}",
+             f"hbm_write_bytes_per_launch = {wr:.0f}",
+             f"hbm_bytes_per_launch = {rd + wr:.0f}",
+             f"algorithmic_bytes_per_launch = {alg}",
+             f"traffic_over_algorithmic = {(rd + wr) / alg:.4f}"]
+    sq_path = os.path.join(d, "sq", "sq_counter_collection.csv")
+    if os.path.exists(sq_path):
+        s = _counters(sq_path)
+        get = lambda c: mean(s[(QUANT_KERNEL, c)])
+        valu = get("SQ_INSTS_VALU")
+        lines += [f"sq_waves = {get('SQ_WAVES'):.0f}",
+                  f"sq_insts_valu = {valu:.0f}   # wave instructions per dispatch",
+                  f"sq_insts_valu_cvt = {get('SQ_INSTS_VALU_CVT'):.0f}",
+                  f"sq_active_inst_valu = {get('SQ_ACTIVE_INST_VALU'):.0f}",
+                  f"sq_wave_cycles = {get('SQ_WAVE_CYCLES'):.0f}",
+                  f"sq_busy_cycles = {get('SQ_BUSY_CYCLES'):.0f}",
+                  f"sq_wait_inst_any = {get('SQ_WAIT_INST_ANY'):.0f}",
+                  f"grbm_gui_active = {get('GRBM_GUI_ACTIVE'):.0f}",
+                  f"valu_lane_insts_per_element = {valu * 64 / n:.2f}",
+                  f"valu_cvt_insts_per_block = {get('SQ_INSTS_VALU_CVT') * 64 / (n // 16):.2f}"]
+    open(COUNTERS, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def other_workloads(fos, synthdata, torch, np, steps=50, warmup=5):
