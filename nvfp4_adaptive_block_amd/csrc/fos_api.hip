@@ -89,6 +89,9 @@ int check_shape(int64_t M, int64_t K, int block) {
   if (M < 0 || K < 0) return fail(FOS_ERR_INVALID_ARG, "negative size M=%lld K=%lld", (long long)M, (long long)K);
   if (K % 16) return fail(FOS_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
   if (block == FOS_BLOCK_16X16 && M % 16) return fail(FOS_ERR_SHAPE, "16x16 blocks need M %% 16 == 0, M=%lld", (long long)M);
+  // a 16x16 unit addresses 16 rows from one base with 32-bit lane offsets
+  if (block == FOS_BLOCK_16X16 && K > (int64_t(1) << 24))
+    return fail(FOS_ERR_SHAPE, "16x16 blocks need K <= 2^24, K=%lld", (long long)K);
   if (K > 0 && M > kMaxElems / K) return fail(FOS_ERR_SHAPE, "M*K exceeds 2^40 elements");
   return FOS_OK;
 }

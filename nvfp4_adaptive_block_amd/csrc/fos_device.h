@@ -128,7 +128,15 @@ __device__ __forceinline__ float div6(float a) {
 
 // RN(x - f32(RN16(xh))): the error of x against the decoded value rounded to
 // binary16 (FP16-error mode).
-__device__ __forceinline__ float sub_f16(float x, float xh) { return x - round_f16(xh); }
+__device__ __forceinline__ float sub_f16(float x, float xh) {
+  // x - f32(h) as one mixed-precision FMA: the product h * -1 is exact and the
+  // FMA rounds once, so this is RN(x - f32(h)) with the same signed zeros
+  // (the compiler turns fma(h, -1, x) back into a convert and a subtract)
+  const _Float16 h = (_Float16)opaque(xh);
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
 
 // ---------------------------------------------------------------- reductions
 
@@ -144,17 +152,35 @@ __device__ __forceinline__ float tree16(float* u) {
   return u[0];
 }
 
+// Cross-lane moves within a DPP row of 16 lanes (register-to-register, no
+// LDS): row_shl:n (lane i reads lane i + n of its row; lanes past the row's
+// end read 0), row_ror:n (rotate within the row) and row_newbcast:n (every
+// lane reads lane n of its row).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowShl = 0x100, kDppRowRor = 0x120, kDppRowBcast = 0x150;
+
 // The same tree across the 16 lanes of a DPP row (lanes 16k .. 16k+15 hold
-// terms 0..15): after it, lane 16k holds the sum; other lanes hold partials.
+// terms 0..15): at each stride s (8, 4, 2, 1) lane i adds lane i + s, so
+// lane 16k ends with the pinned sum; the result is then broadcast to all 16
+// lanes of the row. (Lanes other than 16k add values that never reach it.)
 __device__ __forceinline__ float tree16_lanes(float v) {
-#pragma unroll
-  for (int s = 8; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 16);
-  return v;
+  v = v + dpp<kDppRowShl + 8>(v);
+  v = v + dpp<kDppRowShl + 4>(v);
+  v = v + dpp<kDppRowShl + 2>(v);
+  v = v + dpp<kDppRowShl + 1>(v);
+  return dpp<kDppRowBcast + 0>(v);
 }
 
+// Max over the 16 lanes of a DPP row, on every lane (max is exact and
+// order-free, so rotations serve).
 __device__ __forceinline__ float max16_lanes(float v) {
-#pragma unroll
-  for (int s = 8; s >= 1; s >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, s, 16));
+  v = __builtin_fmaxf(v, dpp<kDppRowRor + 8>(v));
+  v = __builtin_fmaxf(v, dpp<kDppRowRor + 4>(v));
+  v = __builtin_fmaxf(v, dpp<kDppRowRor + 2>(v));
+  v = __builtin_fmaxf(v, dpp<kDppRowRor + 1>(v));
   return v;
 }
 

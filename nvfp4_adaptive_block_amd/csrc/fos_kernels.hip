@@ -329,7 +329,7 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
 // amax is the max over the lanes; each lane sums its row's error terms with
 // the pinned tree, and the lane sums are combined with the same tree in row
 // order. The result (kept candidate) is the same on all 16 lanes.
-template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, bool TAB>
+template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, bool TAB, bool SEQ>
 __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_dec, const Table& tab, BlockOut& o,
                                            float* xh) {
   const float a = max16_lanes(amax16<CAREFUL>(x));
@@ -343,24 +343,41 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
     const float n = any_nan16(x) ? 1.0f : 0.0f;
     return max16_lanes(n) == 0.0f;
   } else {
-    const Cand k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
+    float e6, e4;
     uint32_t c40, c41;
-    encode16<CAREFUL>(x, k4.E, c40, c41);
-    float xh6[16], xh4[16];
-    decode16(c60, c61, k6.D, xh6);
-    decode16(c40, c41, k4.D, xh4);
-    float e6 = tree16_lanes(err16<METRIC, PREC>(x, xh6));
-    float e4 = tree16_lanes(err16<METRIC, PREC>(x, xh4));
-    e6 = __shfl(e6, 0, 16);
-    e4 = __shfl(e4, 0, 16);
+    Cand k4;
+    if (SEQ) {
+      // one candidate after the other (fewer live registers)
+      {
+        float t[16];
+        decode16(c60, c61, k6.D, t);
+        e6 = tree16_lanes(err16<METRIC, PREC>(x, t));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
+      encode16<CAREFUL>(x, k4.E, c40, c41);
+      {
+        float t[16];
+        decode16(c40, c41, k4.D, t);
+        e4 = tree16_lanes(err16<METRIC, PREC>(x, t));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // both at once: the two cross-lane trees interleave, which hides the
+      // DPP read-after-write stalls of each
+      k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
+      encode16<CAREFUL>(x, k4.E, c40, c41);
+      float xh6[16], xh4[16];
+      decode16(c60, c61, k6.D, xh6);
+      decode16(c40, c41, k4.D, xh4);
+      e6 = tree16_lanes(err16<METRIC, PREC>(x, xh6));
+      e4 = tree16_lanes(err16<METRIC, PREC>(x, xh4));
+    }
     const bool four = e4 < e6;
     o.c0 = four ? c40 : c60;
     o.c1 = four ? c41 : c61;
     o.scale = four ? k4.scale : k6.scale;
-    if (NEED_XHAT) {
-#pragma unroll
-      for (int i = 0; i < 16; i++) xh[i] = four ? xh4[i] : xh6[i];
-    }
+    if (NEED_XHAT) decode16(o.c0, o.c1, four ? k4.D : k6.D, xh);
     return CAREFUL || (e6 == e6 && e4 == e4);
   }
 }
@@ -517,7 +534,13 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
       S_dec = 1.0f / S_enc;
       tab.build(S_enc, S_dec, lane);
     }
+    // per-row scales: the row whose global scale is current, its amax bits
+    // (rows of equal amax share the table) and, grouped, the current group's
+    // row range
     int64_t tab_row = -1;
+    int64_t tab_amax = -1;  // amax bits of the current table; -1: none built yet
+    int64_t g_lo = 0, g_hi = 0;
+    int g_cur = -1;
 
     // one unit: quantize the lane's block held in `raw`, store its outputs
     // (two stores). Units past the range compute on zeros and their stores
@@ -526,11 +549,23 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
       if (GRAN != kGranTensor) {
         const int64_t row = pos.row;  // wave-uniform
         if (valid && row != tab_row) {
-          const float A = (GRAN == kGranRow) ? ld_const(T.amax, row)
-                                             : ld_const(args.group_amax, group_of(args.offs, args.G, row));
-          S_enc = global_encode_scale(A, six_b);
-          S_dec = 1.0f / S_enc;
-          tab.build(S_enc, S_dec, lane);
+          float A;
+          if (GRAN == kGranRow) {
+            A = ld_const(T.amax, row);
+          } else {
+            if (row < g_lo || row >= g_hi) {
+              g_cur = group_of(args.offs, args.G, row);
+              g_lo = g_cur ? (int64_t)ld_const(args.offs, g_cur - 1) : 0;
+              g_hi = (g_cur == args.G - 1) ? INT64_MAX : (int64_t)ld_const(args.offs, g_cur);
+            }
+            A = ld_const(args.group_amax, g_cur);
+          }
+          if ((int64_t)__float_as_uint(A) != tab_amax) {
+            S_enc = global_encode_scale(A, six_b);
+            S_dec = 1.0f / S_enc;
+            tab.build(S_enc, S_dec, lane);
+            tab_amax = __float_as_uint(A);
+          }
           tab_row = row;
         }
       }
@@ -586,15 +621,17 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
 
 // ------------------------------------------------------------ 16x16 kernel
 
-// A unit is one 16-row band times four consecutive tiles: lane = 16 * tile +
-// row in tile, so a wave reads 16 rows x 64 columns. Lanes of a ragged last
-// group of tiles idle with out-of-range offsets.
+// A unit is one 16-row band times 4 * kS consecutive tiles: lane = 16 * tile +
+// row in tile for each of the lane's kS segments, so a wave reads 16 rows x
+// 64 * kS columns. Lanes of a ragged last group of tiles idle with
+// out-of-range offsets.
 template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   __shared__ float lds[4][256];
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kEB = kB / 16;  // bytes per element
   constexpr bool kXhat = OUT == kOutQdq;
+  constexpr int kS = tile_segs(OUT, DT);
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const Table tab{lds[wv], lds[wv] + 128};
@@ -602,7 +639,7 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t K = args.K, nbk = K >> 4;
-  const int64_t gpb = (nbk + 3) >> 2;  // groups of four tiles per band
+  const int64_t gpb = (nbk + 4 * kS - 1) / (4 * kS);  // units per band
   const int64_t total = (args.M >> 4) * gpb;
   const int64_t per = (total + nwaves - 1) / nwaves;
   int64_t u = wave * per;
@@ -627,78 +664,113 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
     tab.build(S_enc, S_dec, lane);
   }
   int64_t cur_band = -1;
+  int64_t cur_amax = -1;  // amax bits of the current table; -1: none built yet
   const int64_t x_bytes = args.M * K * kEB;
   const int64_t c_bytes = args.M * K / 2;
   const int64_t s_bytes = args.M * nbk;
 
   struct U16 {
     Rsrc x, out, scl;
-    uint32_t ox, oo, os;  // lane offsets
+    uint32_t ox[kS], oo[kS], os[kS];  // lane offsets of the lane's segments
   };
-  auto unit = [&](int64_t uu, bool valid) {
-    const int64_t band = uu / gpb, tg = uu - band * gpb;
-    const bool active = valid && (tg * 4 + tq < nbk);
-    const int64_t ex = band * 16 * K + tg * 64;  // first element of the unit
+  // Position of a unit: its band and index within the band, advanced
+  // incrementally (no 64-bit division per unit).
+  struct P16 {
+    int64_t band, tg;
+  };
+  // the lane's offsets within a unit (the same for every unit)
+  uint32_t lane_ox[kS], lane_oo[kS], lane_os[kS];
+#pragma unroll
+  for (int j = 0; j < kS; j++) {
+    const uint32_t tl = tq + 4 * j;  // tile within the unit
+    lane_ox[j] = ((uint32_t)r16 * (uint32_t)K + tl * 16) * kEB;
+    lane_oo[j] = (uint32_t)r16 * (uint32_t)(K / 2) + tl * 8;
+    lane_os[j] = (uint32_t)r16 * (uint32_t)nbk + tl;
+  }
+  auto advance = [&](P16 p) {
+    if (++p.tg == gpb) { p.tg = 0; ++p.band; }
+    return p;
+  };
+  auto unit = [&](const P16& p, bool valid) {
+    const int64_t t0 = p.tg * 4 * kS;                 // first tile of the unit
+    const int64_t ex = p.band * 16 * K + t0 * 16;     // its first element
+    const int64_t es = p.band * 16 * nbk + t0;        // its first scale
     U16 r;
     r.x = make_rsrc(static_cast<const char*>(args.x) + ex * kEB, valid ? x_bytes - ex * kEB : 0);
-    r.ox = active ? (uint32_t)((r16 * K + tq * 16) * kEB) : kOOB;
     if (OUT == kOutQuant) {
       r.out = make_rsrc(args.codes + ex / 2, valid ? c_bytes - ex / 2 : 0);
-      r.oo = active ? (uint32_t)(r16 * (K / 2) + tq * 8) : kOOB;
-      const int64_t es = band * 16 * nbk + tg * 4;
       r.scl = make_rsrc(args.scales + es, valid ? s_bytes - es : 0);
-      r.os = active ? (uint32_t)(r16 * nbk + tq) : kOOB;
     } else {
       r.out = make_rsrc(static_cast<char*>(args.y) + ex * kEB, valid ? x_bytes - ex * kEB : 0);
-      r.oo = r.ox;
       r.scl = r.out;
-      r.os = kOOB;
+    }
+#pragma unroll
+    for (int j = 0; j < kS; j++) {
+      const bool active = valid && (t0 + tq + 4 * j < nbk);
+      r.ox[j] = active ? lane_ox[j] : kOOB;
+      r.oo[j] = OUT == kOutQuant ? (active ? lane_oo[j] : kOOB) : r.ox[j];
+      r.os[j] = (OUT == kOutQuant && active) ? lane_os[j] : kOOB;
     }
     return r;
   };
 
-  auto process = [&](const Raw<DT>& raw, int64_t uu, bool valid, const U16& U) {
-    const int64_t band = uu / gpb;
-    if (GRAN == kGranRow && valid && band != cur_band) {
+  auto process = [&](const Raw<DT>* raw, const P16& p, bool valid, const U16& U) {
+    if (GRAN == kGranRow && valid && p.band != cur_band) {
       // tile-uniform contract: the band uses its first row's amax, and a band
       // whose rows differ is flagged
-      const float A = ld_const(args.amax, band * 16);
+      const float A = ld_const(args.amax, p.band * 16);
       bool uniform = true;
 #pragma unroll
-      for (int i = 1; i < 16; i++) uniform &= __float_as_uint(ld_const(args.amax, band * 16 + i)) == __float_as_uint(A);
+      for (int i = 1; i < 16; i++) uniform &= __float_as_uint(ld_const(args.amax, p.band * 16 + i)) == __float_as_uint(A);
       if (!uniform && args.status && lane == 0) atomicOr(args.status, kStatusTileNonuniform);
-      S_enc = global_encode_scale(A, six_b);
-      S_dec = 1.0f / S_enc;
-      tab.build(S_enc, S_dec, lane);
-      cur_band = band;
+      if ((int64_t)__float_as_uint(A) != cur_amax) {
+        S_enc = global_encode_scale(A, six_b);
+        S_dec = 1.0f / S_enc;
+        tab.build(S_enc, S_dec, lane);
+        cur_amax = __float_as_uint(A);
+      }
+      cur_band = p.band;
     }
-    float x[16], xh[16];
-    raw.unpack(x);
-    BlockOut o;
-    if (!tile_16x16<RECIPE, METRIC, PREC, false, kXhat, true>(x, S_enc, S_dec, tab, o, xh))
-      tile_16x16<RECIPE, METRIC, PREC, true, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
-    if (OUT == kOutQuant) {
-      store_codes(U.out, U.oo, o.c0, o.c1);
-      store_scale(U.scl, U.os, o.scale);
-    } else {
-      store16<DT>(U.out, U.oo, xh);
+#pragma unroll
+    for (int j = 0; j < kS; j++) {
+      float x[16], xh[16];
+      raw[j].unpack(x);
+      BlockOut o;
+      if (!tile_16x16<RECIPE, METRIC, PREC, false, kXhat, true, (kS > 1)>(x, S_enc, S_dec, tab, o, xh))
+        tile_16x16<RECIPE, METRIC, PREC, true, kXhat, true, (kS > 1)>(x, S_enc, S_dec, tab, o, xh);
+      if (OUT == kOutQuant) {
+        store_codes(U.out, U.oo[j], o.c0, o.c1);
+        store_scale(U.scl, U.os[j], o.scale);
+      } else {
+        store16<DT>(U.out, U.oo[j], xh);
+      }
     }
   };
 
+  auto load_unit = [&](Raw<DT>* r, const U16& U) {
+#pragma unroll
+    for (int j = 0; j < kS; j++) r[j].load(U.x, U.ox[j]);
+  };
+
   // two units in flight, as in the 1x16 kernel
-  U16 UA = unit(u, true), UB = unit(u + 1, u + 1 < u_end);
-  Raw<DT> A, B;
-  A.load(UA.x, UA.ox);
-  dummy_stores<1>();
-  B.load(UB.x, UB.ox);
+  const int64_t band0 = u / gpb;
+  P16 pa{band0, u - band0 * gpb};
+  P16 pb = advance(pa);
+  U16 UA = unit(pa, true), UB = unit(pb, u + 1 < u_end);
+  Raw<DT> A[kS], B[kS];
+  load_unit(A, UA);
+  dummy_stores<kS>();
+  load_unit(B, UB);
   for (; u < u_end; u += 2) {
     const bool hasB = u + 1 < u_end;
-    process(A, u, true, UA);
-    UA = unit(u + 2, u + 2 < u_end);
-    A.load(UA.x, UA.ox);
-    process(B, u + 1, hasB, UB);
-    UB = unit(u + 3, u + 3 < u_end);
-    B.load(UB.x, UB.ox);
+    process(A, pa, true, UA);
+    pa = advance(pb);
+    UA = unit(pa, u + 2 < u_end);
+    load_unit(A, UA);
+    process(B, pb, hasB, UB);
+    pb = advance(pa);
+    UB = unit(pb, u + 3 < u_end);
+    load_unit(B, UB);
   }
 }
 
@@ -893,7 +965,8 @@ template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 static hipError_t launch_16x16_t(const Args16x16& a, hipStream_t s) {
   auto* fn = &k_16x16<DT, RECIPE, METRIC, PREC, GRAN, OUT>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
-  const int64_t units = (a.M / 16) * ((a.K / 16 + 3) / 4);
+  constexpr int kT = 4 * tile_segs(OUT, DT);
+  const int64_t units = (a.M / 16) * ((a.K / 16 + kT - 1) / kT);
   const int64_t grid = max((int64_t)1, min(resident, (units + 3) / 4));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
