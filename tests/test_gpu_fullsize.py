@@ -1,0 +1,143 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: the whole tensor goes through the library in one call, and
+the oracle recomputes sampled rows (1x16; per-row independence given the
+global scale) or sampled 16-row bands (16x16). Global amaxes are compared in
+full. Every knob combination of each workload is run.
+
+Workloads: the dense activation tensor (bf16 8192x4096, four data families),
+the 16x16 weights (bf16 4096x14336, fp32 4096x4096), the fused-QDQ expert
+list (8 x 2048x7168, bf16 and fp16) and the grouped MoE tokens
+(65536 + 4096 padding rows x 7168, 64 groups).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_adaptive_block_amd as fos
+import synthdata
+from synthdata import raw_bits
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("nvfp4", "mse", "exact")] + [("4over6", m, p) for m in ("mae", "mse") for p in ("exact", "fp16")]
+BOUNDS = (448, 256)
+
+
+def sample_rows(M, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([[0, M - 1], rng.integers(0, M, n), np.asarray(extra, np.int64)])
+    return np.unique(rows.astype(np.int64))
+
+
+def check_amax(orc, x_dev, bits, dtype, gran):
+    got = fos.fos_amax(x_dev, gran)
+    torch.cuda.synchronize()
+    want = orc.amax(bits, dtype, gran)
+    np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32), err_msg=f"amax {gran}")
+    return want
+
+
+# ------------------------------------------------------------------ dense activations
+
+@pytest.mark.parametrize("family", synthdata.ACTIVATION_FAMILIES)
+def test_dense_activation_8192x4096(orc, family):
+    M, K = 8192, 4096
+    seed = 21 + synthdata.ACTIVATION_FAMILIES.index(family)
+    x = synthdata.activation_family(family, M, K, seed, "bf16")
+    bits = raw_bits(x)
+    xd = x.to("cuda")
+    am = {"tensor": check_amax(orc, xd, bits, "bf16", "tensor"), "row": check_amax(orc, xd, bits, "bf16", "row")}
+    rows = sample_rows(M, 48, seed, extra=range(8))
+    codes = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
+    for (recipe, metric, prec), bound, gran in itertools.product(MODES, BOUNDS, ("tensor", "row")):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, scale_gran=gran)
+        a = am[gran]
+        _, _, sdec = fos.fos_quantize(xd, torch.from_numpy(a).to("cuda"), codes=codes, scales=scales, **kw)
+        torch.cuda.synchronize()
+        want = orc.quantize(bits[rows], "bf16", a if gran == "tensor" else a[rows], **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"], err_msg=f"scales {family} {kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"codes {family} {kw}")
+        sd = sdec.cpu().numpy().view(np.uint32)
+        np.testing.assert_array_equal(sd if gran == "tensor" else sd[rows], want["sdec"].view(np.uint32))
+
+
+# ------------------------------------------------------------------ 16x16 weights
+
+@pytest.mark.parametrize("dtype,M,K,seed", [("bf16", 4096, 14336, 31), ("fp32", 4096, 4096, 32)])
+def test_weights_16x16(orc, dtype, M, K, seed):
+    x = synthdata.weight(M, K, seed, dtype)
+    bits = raw_bits(x)
+    xd = x.to("cuda")
+    am = {"tensor": check_amax(orc, xd, bits, dtype, "tensor"), "row": check_amax(orc, xd, bits, dtype, "band16")}
+    bands = np.unique(np.concatenate([[0, M // 16 - 1], np.random.default_rng(seed).integers(0, M // 16, 3)]))
+    rows = (bands[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
+    codes = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for (recipe, metric, prec), bound, gran in itertools.product(MODES, BOUNDS, ("tensor", "row")):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, scale_gran=gran, block="16x16")
+        a = am[gran]
+        fos.fos_quantize(xd, torch.from_numpy(a).to("cuda"), codes=codes, scales=scales, status=status, **kw)
+        torch.cuda.synchronize()
+        want = orc.quantize(bits[rows], dtype, a if gran == "tensor" else a[rows], **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"], err_msg=f"scales {dtype} {kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"codes {dtype} {kw}")
+    assert int(status.item()) == 0  # band amaxes are uniform within each tile
+
+
+# ------------------------------------------------------------------ fused QDQ over the expert list
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_qdq_expert_list_8x2048x7168(orc, dtype):
+    lst = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=(dtype,))[dtype]
+    bits = [raw_bits(t) for t in lst]
+    xs = [t.to("cuda") for t in lst]
+    ams = [orc.amax(b, dtype, "tensor") for b in bits]
+    ams_d = [torch.from_numpy(a).to("cuda") for a in ams]
+    ys = [torch.empty_like(t) for t in xs]
+    rows = [sample_rows(2048, 12, 100 + i) for i in range(8)]
+    for (recipe, metric, prec), bound in itertools.product(MODES, BOUNDS):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+        fos.fos_qdq_list(xs, ams_d, outs=ys, **kw)
+        torch.cuda.synchronize()
+        for i in range(8):
+            want = orc.qdq(bits[i][rows[i]], dtype, ams[i], **kw)
+            got = raw_bits(ys[i].cpu())[rows[i]]
+            np.testing.assert_array_equal(got, want, err_msg=f"tensor {i} {kw}")
+
+
+# ------------------------------------------------------------------ grouped MoE tokens
+
+def test_grouped_moe_65536x7168(orc):
+    M, pad, K, G = 65536, 4096, 7168, 64
+    x, offs, _ = synthdata.grouped_tokens(M, pad, K, G)
+    bits = raw_bits(x)
+    starts = np.concatenate([[0], offs[:-1]]).astype(np.int64)
+    gam = np.array([orc.amax(bits[s:e], "bf16", "tensor")[0] if e > s else 0.0 for s, e in zip(starts, offs)],
+                   np.float32)
+    group_of_row = np.searchsorted(offs, np.arange(M), side="right")
+    edges = [r for s, e in zip(starts, offs) if e > s for r in (s, e - 1)]
+    rows = sample_rows(M, 96, 55, extra=edges)
+    xd = x.to("cuda")
+    codes = torch.empty(M + pad, K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M + pad, K // 16, dtype=torch.uint8, device="cuda")
+    gsdec = torch.empty(G, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for bound in BOUNDS:
+        kw = dict(recipe="4over6", err_metric="mse", err_prec="exact", bound=bound)
+        fos.fos_quantize_grouped(xd, torch.from_numpy(offs).to("cuda"), torch.from_numpy(gam).to("cuda"),
+                                 codes=codes, scales=scales, group_sdec=gsdec, status=status, **kw)
+        torch.cuda.synchronize()
+        # rows of group g quantize like a per-row tensor whose row amax is A_g
+        want = orc.quantize(bits[rows], "bf16", gam[group_of_row[rows]], scale_gran="row", **kw)
+        c = codes.cpu().numpy()
+        s = scales.cpu().numpy()
+        np.testing.assert_array_equal(s[rows], want["scales"], err_msg=f"scales bound {bound}")
+        np.testing.assert_array_equal(c[rows], want["codes"], err_msg=f"codes bound {bound}")
+        assert not c[M:].any() and not s[M:].any(), "padding rows must be zero"
+        want_sdec = np.array([orc.global_decode_scale(float(a), bound) for a in gam], np.float32)
+        np.testing.assert_array_equal(gsdec.cpu().numpy().view(np.uint32), want_sdec.view(np.uint32))
+        assert int(status.item()) == 0
