@@ -4,16 +4,18 @@
 One step is one pass of the hot path over the dense-activation workload
 (bf16 8192x4096 drawn from N(0,1), 1x16 blocks, per-tensor global scale,
 four-over-six with MSE exact error, E4M3 bound 448): the NaN-dropping tensor
-amax (fos_amax) and the quantize kernel (fos_quantize) writing packed E2M1
-codes and E4M3 scales. Inputs rotate over enough resident copies that the
-footprint exceeds the 256 MB Infinity Cache, so every step reads from HBM.
+amax and the quantize writing packed E2M1 codes and E4M3 scales, in one
+launch (fos_quantize_fused). Inputs rotate over enough resident copies that
+the footprint exceeds the 256 MB Infinity Cache, so every step reads from HBM.
 
 `value` is the step's algorithmic HBM traffic (amax read 2 B/elem plus
 quantize 2 + 0.5 + 1/16 B/elem) over the measured step time. The `roofline`
-object covers the quantize kernel alone, timed with HIP events on the stream
-it runs on. `cpu_baseline` times the CPU oracle on the same workload. Other
-configurations (16x16 weights, the fused-QDQ expert list, the grouped MoE
-tensor) are timed briefly and reported under `other_workloads`.
+object covers the step's kernel, timed with HIP events on the stream it runs
+on. `cpu_baseline` times the CPU oracle on the same workload. The quantize
+kernel alone with a precomputed amax (the pages' kernel metric), the
+two-launch step and the other configurations (16x16 weights, the fused-QDQ
+expert list, the grouped MoE tensor) are timed briefly and reported under
+`other_workloads`.
 
 Prints exactly one JSON line on stdout.
 """
@@ -33,7 +35,17 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 << 20
 FOOTPRINT = 1 << 30            # rotate buffers up to >= 1 GiB
 METRIC = "4over6 quantize/QDQ achieved HBM GB/s and % of MI355X peak (bit-exact)"
-COUNTERS = os.path.join(ROOT, "profiles", "quantize_1x16_bf16_8192x4096_counters.txt")
+FUSED_KERNEL = "void fos::k_fused<0, 1, 1, 0>(fos::Args1x16<1>, unsigned int*, float*)"
+QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0>(fos::Args1x16<1>)"
+COPY_BYTES = 256 << 20         # the profile pass's calibration copy
+# counter summaries per kernel: (file, readable workload, algorithmic bytes per launch)
+_N = 8192 * 4096
+COUNTER_FILES = {
+    FUSED_KERNEL: (os.path.join(ROOT, "profiles", "fused_amax_quantize_bf16_8192x4096_counters.txt"),
+                   "fos_quantize_fused: per-tensor amax and quantize in one launch", _N * 2 + _N * 2 + _N // 2 + _N // 16),
+    QUANT_KERNEL: (os.path.join(ROOT, "profiles", "quantize_1x16_bf16_8192x4096_counters.txt"),
+                   "fos_quantize with a precomputed amax", _N * 2 + _N // 2 + _N // 16),
+}
 KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_adaptive_block_amd", "csrc", f)
                   for f in ("fos_kernels.hip", "fos_device.h", "fos_kernels.h")]
 
@@ -67,22 +79,10 @@ def read_profile_value(path, key):
         return None
 
 
-def read_counters():
-    """HBM bytes per quantize launch from the committed rocprofv3 counter
+def read_counters(kernel):
+    """HBM bytes per launch of `kernel` from its committed rocprofv3 counter
     summary, or None when it is missing or was taken on other kernel code."""
-    if not os.path.exists(COUNTERS):
-        return None
-    kv = {}
-    for line in open(COUNTERS):
-        if "=" in line and not line.lstrip().startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    return read_profile_value(COUNTER_FILES[kernel][0], "hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -162,53 +162,54 @@ def main():
     amax = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(nset)]
     log(f"[bench] {nset} rotating buffer sets ({nset * (in_bytes + out_bytes) / 2**30:.2f} GiB)")
 
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=amax[i], sdec=sdec[i], workspace=ws,
+                               status=status, **knobs)
+
     if args.profile_pass:
-        # a few launches of each kernel, plus a plain copy of known size for
-        # calibrating the HBM counters
+        # a few launches of the step's kernel and of the separate amax and
+        # quantize kernels, plus a plain copy of known size for calibrating
+        # the HBM counters
+        for i in range(8):
+            step(i % nset)
         for i in range(8):
             fos.fos_amax(xs[i % nset], "tensor", out=amax[i % nset])
             fos.fos_quantize(xs[i % nset], amax[i % nset], codes=codes[i % nset], scales=scales[i % nset],
                              sdec=sdec[i % nset], **knobs)
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(4):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log("[bench] profile pass done (copy kernel: 268435456 bytes read and written per launch)")
+        log(f"[bench] profile pass done (copy kernel: {COPY_BYTES} bytes read and written per launch)")
         return
 
     # ---------------------------------------------------------------- main step
-    def step(i, ev_q=None):
-        fos.fos_amax(xs[i], "tensor", out=amax[i])
-        if ev_q is not None:
-            ev_q.record()
-        fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)
-
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
     for i in range(args.warmup):
         step(i % nset)
     torch.cuda.synchronize()
-    # events: marks[i] opens step i (and closes step i-1's quantize), qs[i]
-    # separates step i's amax from its quantize
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    qs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # the step is one kernel launch: two events on the launch stream bracket
+    # the timed region, and the kernel's average launch time is the region's
+    # time over the step count (per-step events would add their own packets)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
     for i in range(args.steps):
-        marks[i].record()
-        step((args.warmup + i) % nset, qs[i])
-    marks[-1].record()
+        step((args.warmup + i) % nset)
+    end.record()
     torch.cuda.synchronize()
-    total_ms = marks[0].elapsed_time(marks[-1])
-    a_ms = [marks[i].elapsed_time(qs[i]) for i in range(args.steps)]
-    q_ms = [qs[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    q_avg_ms = float(np.mean(q_ms))
-    a_avg_ms = float(np.mean(a_ms))
-    step_bytes = n * 2 + n * 2 + out_bytes          # amax read + quantize read + write
-    q_bytes = in_bytes + out_bytes
+    k_avg_ms = ms_per_step
+    barrier_ok = int(status.item()) == 0
+    step_bytes = n * 2 + in_bytes + out_bytes       # amax read + quantize read + write (per element 2 + 2.5625 B)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    q_gbs = q_bytes / (q_avg_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s); quantize {q_avg_ms * 1e3:.1f} us "
-        f"({q_gbs:.0f} GB/s, {q_gbs / PEAK_HBM_GBS:.1%} of peak); amax {a_avg_ms * 1e3:.1f} us")
+    k_gbs = step_bytes / (k_avg_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s); fused kernel {k_avg_ms * 1e3:.1f} us "
+        f"({k_gbs:.0f} GB/s, {k_gbs / PEAK_HBM_GBS:.1%} of peak); barrier ok: {barrier_ok}")
 
     # bit-exact spot check of the last outputs against the CPU oracle
     bit_exact = None
@@ -250,10 +251,10 @@ def main():
     # ---------------------------------------------------------------- other workloads
     other = {}
     if not args.no_other:
-        other = other_workloads(fos, synthdata, torch, np)
+        other = other_workloads(fos, synthdata, torch, np, c2=(xs, codes, scales, amax, sdec, knobs))
 
-    traffic = read_counters()
-    rocprof_us = read_profile_value(KERNEL_TRACE, "quantize_kernel_avg_us")
+    traffic = read_counters(FUSED_KERNEL)
+    rocprof_us = read_profile_value(KERNEL_TRACE, "fused_kernel_avg_us")
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -268,17 +269,17 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "dense activation quantize, bf16 8192x4096 N(0,1) seed 21, 1x16 blocks, "
-                               "per-tensor amax (fos_amax) + four-over-six MSE exact, E4M3 bound 448",
+                               "per-tensor amax + four-over-six MSE exact, E4M3 bound 448, in one launch "
+                               "(fos_quantize_fused)",
                    "M": M, "K": K, "input_dtype": "bf16", "recipe": "4over6", "err_metric": "mse",
                    "err_prec": "exact", "e4m3_bound": 448, "rotating_sets": nset,
                    "step_bytes": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "fos_quantize (k_1x16, bf16, 4over6 MSE exact)",
-                     "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(q_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": q_bytes, "avg_launch_us": round(q_avg_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "fos_quantize_fused (k_fused, bf16, 4over6 MSE exact)",
+                     "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": round(k_avg_ms * 1e3, 2),
                      "rocprof_kernel_avg_us": rocprof_us},
-        "amax_kernel": {"avg_launch_us": round(a_avg_ms * 1e3, 2),
-                        "achieved_GBs": round(in_bytes / (a_avg_ms * 1e-3) / 1e9, 1)},
+        "barrier_ok": barrier_ok,
         "bit_exact_sample": bit_exact,
         "cpu_baseline": cpu,
         "other_workloads": other,
@@ -288,8 +289,6 @@ def main():
 
 # ---------------------------------------------------------------- profile summaries
 
-QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0>(fos::Args1x16<1>)"
-COPY_BYTES = 256 << 20     # the profile pass's calibration copy
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o kt -- "
           "python3 $REPO/bench.py --steps 200 --warmup 20 --no-cpu-baseline",
@@ -325,6 +324,11 @@ def describe_kernel(name: str) -> str:
         return f"16x16 {_OUT[out]} {_DT[dt]} {_RC[rc]}{err} {_GR[gr]}"
     if "k_amax_tensor" in name:
         return "amax per tensor (" + {"0": "bf16", "1": "fp16", "2": "fp32"}.get(name.split("<")[1][0], "?") + ")"
+    if "k_fused" in name:
+        m = re.match(r"void fos::k_fused<(\d), (\d), (\d), (\d)>", name)
+        dt, rc, mt, pr = m.groups()
+        err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
+        return f"fused amax + 1x16 quantize {_DT[dt]} {_RC[rc]}{err} tensor"
     if "k_zero_u32" in name:
         return "clear the amax word"
     if "copyBuffer" in name:
@@ -344,8 +348,9 @@ def _counters(path):
 
 
 def write_profiles(d):
-    """Write profiles/kernel_trace_bench_workloads.txt and the quantize kernel's
-    counter summary from the CSV files rocprofv3 wrote under d."""
+    """Write profiles/kernel_trace_bench_workloads.txt and the counter
+    summaries of the step's fused kernel and of the precomputed-amax quantize
+    kernel from the CSV files rocprofv3 wrote under d."""
     import csv
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
@@ -359,80 +364,104 @@ def write_profiles(d):
              f"# kernel_source_sha256_16 = {ksha}",
              "# durations in microseconds, per dispatch",
              f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>6}  mode / kernel"]
-    q_avg = None
+    avg = {}
     for r in stats:
         name = r["Name"]
-        if name == QUANT_KERNEL:
-            q_avg = float(r["AverageNs"]) / 1e3
+        avg[name] = float(r["AverageNs"]) / 1e3
         desc = describe_kernel(name)
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):5.1f}%  "
                      f"{desc + ' | ' if desc else ''}{name[:110]}")
-    if q_avg is not None:
-        lines.append(f"quantize_kernel_avg_us = {q_avg:.2f}   # {describe_kernel(QUANT_KERNEL)}, the bench step's kernel")
+    if FUSED_KERNEL in avg:
+        lines.append(f"fused_kernel_avg_us = {avg[FUSED_KERNEL]:.2f}   # the bench step's one kernel")
+    if QUANT_KERNEL in avg:
+        lines.append(f"quantize_kernel_avg_us = {avg[QUANT_KERNEL]:.2f}   # bf16 8192x4096 quantize, precomputed amax")
     open(os.path.join(out_dir, "kernel_trace_bench_workloads.txt"), "w").write("\n".join(lines) + "\n")
 
-    # HBM counters of the quantize kernel, calibrated on a copy of known size
+    # HBM counters, calibrated on a copy of known size
     f = _counters(os.path.join(d, "fetch", "fetch_counter_collection.csv"))
     w = _counters(os.path.join(d, "write", "write_counter_collection.csv"))
+    sq_path = os.path.join(d, "sq", "sq_counter_collection.csv")
+    s = _counters(sq_path) if os.path.exists(sq_path) else None
     copy_name = "__amd_rocclr_copyBuffer"
-    cf = f[(copy_name, "FETCH_SIZE")][-4:]   # the profile pass ends with four 256 MiB copies
+    cf = f[(copy_name, "FETCH_SIZE")][-4:]   # the profile pass ends with four copies of COPY_BYTES
     cw = w[(copy_name, "WRITE_SIZE")][-4:]
-    qf = f[(QUANT_KERNEL, "FETCH_SIZE")]
-    qw = w[(QUANT_KERNEL, "WRITE_SIZE")]
     mean = lambda v: sum(v) / len(v)
     fetch_factor = COPY_BYTES / (mean(cf) * 1024)
     write_factor = COPY_BYTES / (mean(cw) * 1024)
-    rd = mean(qf) * 1024 * fetch_factor
-    wr = mean(qw) * 1024 * write_factor
-    n = 8192 * 4096
-    alg = n * 2 + n // 2 + n // 16
-    lines = ["# rocprofv3 counter summary: fos_quantize, 1x16 blocks, bf16 8192x4096 N(0,1), four-over-six MSE exact,",
-             "# E4M3 bound 448, per-tensor scale (the bench step's quantize kernel)",
-             "# commands (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):",
-             "#   " + PROFILE_CMDS["fetch"], "#   " + PROFILE_CMDS["write"], "#   " + PROFILE_CMDS["sq"],
-             f"#   python3 $REPO/bench.py --write-profiles $OUT",
-             "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch. The factors scale them to bytes so that the",
-             f"# profile pass's plain copy of {COPY_BYTES} bytes reads and writes exactly that many bytes.",
-             f"kernel = {QUANT_KERNEL}",
-             f"kernel_source_sha256_16 = {ksha}",
-             f"dispatches = {len(qf)}",
-             f"fetch_size_kib = {mean(qf):.1f}",
-             f"write_size_kib = {mean(qw):.1f}",
-             f"copy_fetch_size_kib = {mean(cf):.1f}",
-             f"copy_write_size_kib = {mean(cw):.1f}",
-             f"fetch_factor = {fetch_factor:.4f}",
-             f"write_factor = {write_factor:.4f}",
-             f"hbm_read_bytes_per_launch = {rd:.0f}",
-             f"hbm_write_bytes_per_launch = {wr:.0f}",
-             f"hbm_bytes_per_launch = {rd + wr:.0f}",
-             f"algorithmic_bytes_per_launch = {alg}",
-             f"traffic_over_algorithmic = {(rd + wr) / alg:.4f}"]
-    sq_path = os.path.join(d, "sq", "sq_counter_collection.csv")
-    if os.path.exists(sq_path):
-        s = _counters(sq_path)
-        get = lambda c: mean(s[(QUANT_KERNEL, c)])
-        valu = get("SQ_INSTS_VALU")
-        lines += [f"sq_waves = {get('SQ_WAVES'):.0f}",
-                  f"sq_insts_valu = {valu:.0f}   # wave instructions per dispatch",
-                  f"sq_insts_valu_cvt = {get('SQ_INSTS_VALU_CVT'):.0f}",
-                  f"sq_active_inst_valu = {get('SQ_ACTIVE_INST_VALU'):.0f}",
-                  f"sq_wave_cycles = {get('SQ_WAVE_CYCLES'):.0f}",
-                  f"sq_busy_cycles = {get('SQ_BUSY_CYCLES'):.0f}",
-                  f"sq_wait_inst_any = {get('SQ_WAIT_INST_ANY'):.0f}",
-                  f"grbm_gui_active = {get('GRBM_GUI_ACTIVE'):.0f}",
-                  f"valu_lane_insts_per_element = {valu * 64 / n:.2f}",
-                  f"valu_cvt_insts_per_block = {get('SQ_INSTS_VALU_CVT') * 64 / (n // 16):.2f}"]
-    open(COUNTERS, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    n = _N
+    for kernel, (path, what, alg) in COUNTER_FILES.items():
+        qf = f[(kernel, "FETCH_SIZE")]
+        qw = w[(kernel, "WRITE_SIZE")]
+        rd = mean(qf) * 1024 * fetch_factor
+        wr = mean(qw) * 1024 * write_factor
+        lines = [f"# rocprofv3 counter summary: {what}; 1x16 blocks, bf16 8192x4096 N(0,1), four-over-six",
+                 "# MSE exact, E4M3 bound 448, per-tensor scale",
+                 "# commands (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):",
+                 "#   " + PROFILE_CMDS["fetch"], "#   " + PROFILE_CMDS["write"], "#   " + PROFILE_CMDS["sq"],
+                 "#   python3 $REPO/bench.py --write-profiles $OUT",
+                 "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch. The factors scale them to bytes so that the",
+                 f"# profile pass's plain copy of {COPY_BYTES} bytes reads and writes exactly that many bytes.",
+                 f"kernel = {kernel}",
+                 f"kernel_source_sha256_16 = {ksha}",
+                 f"dispatches = {len(qf)}",
+                 f"fetch_size_kib = {mean(qf):.1f}",
+                 f"write_size_kib = {mean(qw):.1f}",
+                 f"copy_fetch_size_kib = {mean(cf):.1f}",
+                 f"copy_write_size_kib = {mean(cw):.1f}",
+                 f"fetch_factor = {fetch_factor:.4f}",
+                 f"write_factor = {write_factor:.4f}",
+                 f"hbm_read_bytes_per_launch = {rd:.0f}",
+                 f"hbm_write_bytes_per_launch = {wr:.0f}",
+                 f"hbm_bytes_per_launch = {rd + wr:.0f}",
+                 f"algorithmic_bytes_per_launch = {alg}",
+                 f"traffic_over_algorithmic = {(rd + wr) / alg:.4f}"]
+        if s is not None and (kernel, "SQ_INSTS_VALU") in s:
+            get = lambda c: mean(s[(kernel, c)])
+            valu = get("SQ_INSTS_VALU")
+            lines += [f"sq_waves = {get('SQ_WAVES'):.0f}",
+                      f"sq_insts_valu = {valu:.0f}   # wave instructions per dispatch",
+                      f"sq_insts_valu_cvt = {get('SQ_INSTS_VALU_CVT'):.0f}",
+                      f"sq_active_inst_valu = {get('SQ_ACTIVE_INST_VALU'):.0f}",
+                      f"sq_wave_cycles = {get('SQ_WAVE_CYCLES'):.0f}",
+                      f"sq_busy_cycles = {get('SQ_BUSY_CYCLES'):.0f}",
+                      f"sq_wait_inst_any = {get('SQ_WAIT_INST_ANY'):.0f}",
+                      f"grbm_gui_active = {get('GRBM_GUI_ACTIVE'):.0f}",
+                      f"valu_lane_insts_per_element = {valu * 64 / n:.2f}",
+                      f"valu_cvt_insts_per_block = {get('SQ_INSTS_VALU_CVT') * 64 / (n // 16):.2f}"]
+        open(path, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
 
 
-def other_workloads(fos, synthdata, torch, np, steps=50, warmup=5):
-    """Brief kernel-only timings of the other configurations (precomputed amax)."""
+def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
+    """Brief kernel-only timings of the other configurations (precomputed
+    amax); each figure is the median launch of its loop."""
     out = {}
 
     def gbs(nbytes, ms):
         return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    # the dense activation tensor: the quantize kernel alone with a
+    # precomputed amax (the pages' kernel metric), and the two-launch step
+    xs, codes, scales, amax, sdec, knobs = c2
+    n = xs[0].numel()
+    qb = n * 2 + n // 2 + n // 16
+    for i in range(len(xs)):
+        fos.fos_amax(xs[i], "tensor", out=amax[i])
+    _, ms = time_loop(lambda i: fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i],
+                                                 **knobs), len(xs), 200, 10)
+    avg = float(np.median(ms))
+    out["quantize_1x16_bf16_8192x4096_precomputed_amax"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
+                                                            "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
+    log(f"[bench] quantize bf16 8192x4096, precomputed amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
+
+    def two_launches(i):
+        fos.fos_amax(xs[i], "tensor", out=amax[i])
+        fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)
+    _, ms = time_loop(two_launches, len(xs), 200, 10)
+    avg = float(np.median(ms))
+    out["amax_then_quantize_bf16_8192x4096"] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb + 2 * n, avg)}
+    log(f"[bench] fos_amax + fos_quantize (two launches): {avg * 1e3:.1f} us")
 
     # 16x16 weights, bf16 4096x14336 and fp32 4096x4096, per-tensor, MSE exact, 448
     for dtype, (M, K) in (("bf16", (4096, 14336)), ("fp32", (4096, 4096))):
@@ -447,7 +476,7 @@ def other_workloads(fos, synthdata, torch, np, steps=50, warmup=5):
         _, ms = time_loop(lambda i: fos.fos_quantize(ws[i], a, codes=c, scales=s, sdec=sd, recipe="4over6",
                                                      block="16x16", err_metric="mse", err_prec="exact"),
                           len(ws), steps, warmup)
-        avg = float(np.mean(ms))
+        avg = float(np.median(ms))
         out[f"quantize_16x16_{dtype}_{M}x{K}"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
                                                   "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
         log(f"[bench] 16x16 {dtype} {M}x{K}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
@@ -465,7 +494,7 @@ def other_workloads(fos, synthdata, torch, np, steps=50, warmup=5):
             r, m, p, bnd = mode
             _, ms = time_loop(lambda i: fos.fos_qdq_list(xs, ams, outs=ys, recipe=r, err_metric=m, err_prec=p,
                                                          bound=bnd), 1, steps, warmup)
-            avg = float(np.mean(ms))
+            avg = float(np.median(ms))
             key = f"qdq_list_8x2048x7168_{dtype}_{r}" + ("" if r == "nvfp4" else f"_{m}_{p}_{bnd}")
             out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
                         "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
@@ -488,7 +517,7 @@ def other_workloads(fos, synthdata, torch, np, steps=50, warmup=5):
         _, ms = time_loop(lambda i: fos.fos_quantize_grouped(x, offs_d, gam, codes=c, scales=s, recipe="4over6",
                                                              err_metric="mse", err_prec="exact", bound=bnd),
                           1, steps, warmup)
-        avg = float(np.mean(ms))
+        avg = float(np.median(ms))
         key = f"quantize_grouped_{M}+{pad}x{K}_G{G}_{bnd}"
         out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
                     "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}

@@ -99,6 +99,10 @@ extern "C" {
 /* device status bits */
 #define FOS_STATUS_TILE_NONUNIFORM 1 /* 16x16 with a per-row amax that differs within a 16-row band */
 #define FOS_STATUS_BAD_OFFS 2        /* group offsets not monotone, not multiples of 16, or past M_alloc */
+#define FOS_STATUS_BARRIER_TIMEOUT 4 /* fos_quantize_fused: the grid barrier did not complete (workspace not zero) */
+
+/* Bytes of the device workspace fos_quantize_fused needs. */
+#define FOS_FUSED_WORKSPACE_BYTES 16384
 
 typedef struct fos_config {
     int32_t recipe;     /* FOS_RECIPE_* */
@@ -177,6 +181,34 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t M, int
 int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
                          const float* group_amax, const fos_config* cfg, uint8_t* codes, uint8_t* scales,
                          float* group_sdec_out, int32_t* d_status, void* stream);
+
+/* Per-tensor amax and quantize in one launch: the amax pre-pass that the
+ * Megatron-LM PR runs as a separate FP32 torch reduction ("What does this PR
+ * do?", fused data path) folded into the quantizer of the pytorch/ao PR
+ * (recipe commit). The result equals fos_amax(..., FOS_AMAX_TENSOR) followed
+ * by fos_quantize with that amax, bit for bit. cfg must be 1x16 with
+ * FOS_PER_TENSOR.
+ *   amax_out:  nullable device float[1], receives the NaN-dropping max |x|.
+ *   sdec_out:  nullable device float[1], receives S_dec.
+ *   workspace: device memory of FOS_FUSED_WORKSPACE_BYTES, 4-byte aligned,
+ *              all zero before its first use (e.g. cleared once at
+ *              allocation). Every completed call leaves its counters zero
+ *              again (only the first 256 bytes, a call counter and the last
+ *              amax, keep changing), so one workspace serves any number of
+ *              calls made one after another; calls that may run at the same time (different
+ *              streams) need workspaces of their own.
+ *   d_status:  nullable device int32; FOS_STATUS_BARRIER_TIMEOUT is set if
+ *              the launch's grid-wide barrier does not complete within a
+ *              bounded number of polls (about a second), in which case the
+ *              codes and scales are incomplete. That happens only with a
+ *              workspace that was not zero, or when other long-running work
+ *              keeps part of the launch from becoming resident (the launch
+ *              holds exactly as many workgroups as fit on the device; two
+ *              fused calls on different streams can starve each other).
+ *              Callers that may overlap fused calls should pass d_status. */
+int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
+                       uint8_t* scales, float* amax_out, float* sdec_out, void* workspace, int32_t* d_status,
+                       void* stream);
 
 #ifdef __cplusplus
 }

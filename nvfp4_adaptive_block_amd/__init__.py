@@ -28,6 +28,8 @@ AMAX_GRANS = {"tensor": 0, "row": 1, "band16": 2}
 
 STATUS_TILE_NONUNIFORM = 1
 STATUS_BAD_OFFS = 2
+STATUS_BARRIER_TIMEOUT = 4
+FUSED_WORKSPACE_BYTES = 16384  # FOS_FUSED_WORKSPACE_BYTES
 
 
 class FosError(RuntimeError):
@@ -59,6 +61,7 @@ _SIGS = {
     "fos_qdq_list": (_I, [_I, _P, _I, ctypes.POINTER(_Config), _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _I64, _I64, _P, _I, _I, _P, _P]),
     "fos_quantize_grouped": (_I, [_P, _I, _I64, _I64, _P, _I, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
+    "fos_quantize_fused": (_I, [_P, _I, _I64, _I64, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -140,6 +143,44 @@ def fos_quantize(x: torch.Tensor, amax: torch.Tensor, *, codes=None, scales=None
         _check(load_library().fos_quantize(_ptr(x), DTYPES[x.dtype], M, K, _ptr(amax), ctypes.byref(cfg),
                                            _ptr(codes), _ptr(scales), _ptr(sdec), _ptr(status), _stream(dev)))
     return codes, scales, sdec
+
+
+_workspaces: dict = {}
+
+
+def fused_workspace(device) -> torch.Tensor:
+    """The zero-initialised workspace fos_quantize_fused uses on `device` when
+    the caller passes none (one per device; calls on one device's streams
+    that may overlap need workspaces of their own)."""
+    dev = torch.device(device)
+    if dev not in _workspaces:
+        _workspaces[dev] = torch.zeros(FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    return _workspaces[dev]
+
+
+def fos_quantize_fused(x: torch.Tensor, *, codes=None, scales=None, amax=None, sdec=None, status=None,
+                       workspace=None, **knobs):
+    """Per-tensor amax and quantize in one launch. Returns (codes, scales,
+    amax float32[1], sdec float32[1])."""
+    _need(x, "x")
+    M, K = x.shape
+    cfg = config(**knobs)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    if sdec is None:
+        sdec = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = fused_workspace(dev)
+    with torch.cuda.device(dev):
+        _check(load_library().fos_quantize_fused(_ptr(x), DTYPES[x.dtype], M, K, ctypes.byref(cfg), _ptr(codes),
+                                                 _ptr(scales), _ptr(amax), _ptr(sdec), _ptr(workspace),
+                                                 _ptr(status), _stream(dev)))
+    return codes, scales, amax, sdec
 
 
 def fos_qdq(x: torch.Tensor, amax: torch.Tensor, *, out=None, **knobs) -> torch.Tensor:

@@ -107,6 +107,8 @@ void mode_of(const fos_config* c, int& metric, int& prec) {
 
 }  // namespace
 
+static_assert(FOS_FUSED_WORKSPACE_BYTES == fos::kFusedWorkspaceBytes, "workspace size mismatch");
+
 extern "C" {
 
 int fos_abi_version(void) { return FOS_ABI_VERSION; }
@@ -300,6 +302,38 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
   a.offs = offs;
   a.group_amax = group_amax;
   return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, fos::kGranGroup, a, s));
+}
+
+int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
+                       uint8_t* scales, float* amax_out, float* sdec_out, void* workspace, int32_t* d_status,
+                       void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
+    return fail(FOS_ERR_CONFIG, "fused amax + quantize supports 1x16 blocks with a per-tensor scale");
+  if ((rc = check_shape(M, K, FOS_BLOCK_1X16))) return rc;
+  if (M * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (!aligned(x, 16) || !aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "x or codes misaligned");
+  if (!aligned(workspace, 4) || !aligned(amax_out, 4) || !aligned(sdec_out, 4) || !aligned(d_status, 4))
+    return fail(FOS_ERR_ALIGN, "workspace/amax/sdec/status misaligned");
+  if ((rc = check_device())) return rc;
+  int metric, prec;
+  mode_of(cfg, metric, prec);
+  fos::Args1x16<1> a;
+  memset(&a, 0, sizeof a);
+  a.t[0] = fos::TensorRef{x, nullptr, nullptr, M, K > 0 ? K : 16, 0};
+  a.n = 1;
+  const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
+  a.total_units = (M * (K / 16) + ub - 1) / ub;
+  a.six_b = six_b(cfg);
+  a.codes = codes;
+  a.scales = scales;
+  a.sdec_out = sdec_out;
+  a.status = d_status;
+  return launch_status(fos::launch_fused(dtype, cfg->recipe, metric, prec, a, static_cast<uint32_t*>(workspace),
+                                         amax_out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

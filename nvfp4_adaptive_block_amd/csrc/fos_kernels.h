@@ -15,7 +15,10 @@ enum { kErrExact = 0, kErrFP16 = 1 };
 enum { kGranTensor = 0, kGranRow = 1, kGranGroup = 2 };
 enum { kOutQuant = 0, kOutQdq = 1 };
 enum { kAmaxTensor = 0, kAmaxRow = 1, kAmaxBand16 = 2 };
-enum { kStatusTileNonuniform = 1, kStatusBadOffs = 2 };
+enum { kStatusTileNonuniform = 1, kStatusBadOffs = 2, kStatusBarrier = 4 };
+
+// Bytes of the fused kernel's workspace (its grid barrier's counters).
+constexpr int kFusedWorkspaceBytes = 16384;
 
 // Tensors per launch of the list kernel (the descriptors travel in the
 // kernel arguments, 48 B each).
@@ -77,6 +80,8 @@ struct Args16x16 {
 
 hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a,
                              hipStream_t s);
+hipError_t launch_fused(int dt, int recipe, int metric, int prec, const Args1x16<1>& a, uint32_t* ws,
+                        float* amax_out, hipStream_t s);
 hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, hipStream_t s);
 hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, hipStream_t s);
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,

@@ -496,26 +496,16 @@ struct Walk {
   }
 };
 
-template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
-__global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
-  __shared__ float lds[4][256];
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const Table tab{lds[wv], lds[wv] + 128};
+// The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED (per-
+// tensor scale only) the global amax is `fused_amax` rather than the
+// tensor's amax in memory.
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT, bool FUSED>
+__device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
+                                          int64_t u_end, float fused_amax) {
   constexpr bool kXhat = OUT == kOutQdq;
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kNB = unit_blocks(OUT, DT) / 64;
-
-  if (OUT == kOutQuant) side_outputs<GRAN>(args);
-
-  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t total = args.total_units;
-  const int64_t per = (total + nwaves - 1) / nwaves;
-  int64_t u = wave * per;
-  const int64_t u_end = min(total, u + per);
-  if (u >= u_end) return;
-
   int ti = 0;
   while (ti + 1 < args.n && args.t[ti + 1].unit_begin <= u) ti++;
   const float six_b = args.six_b;
@@ -530,7 +520,7 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
 
     float S_enc = 1.0f, S_dec = 1.0f;
     if (GRAN == kGranTensor) {
-      S_enc = global_encode_scale(ld_const(T.amax, 0), six_b);
+      S_enc = global_encode_scale(FUSED ? fused_amax : ld_const(T.amax, 0), six_b);
       S_dec = 1.0f / S_enc;
       tab.build(S_enc, S_dec, lane);
     }
@@ -617,6 +607,24 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
     if (u >= u_end) break;
     ti++;
   }
+}
+
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
+__global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
+  __shared__ float lds[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+
+  if (OUT == kOutQuant) side_outputs<GRAN>(args);
+
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
+  const int64_t u = wave * per;
+  const int64_t u_end = min(args.total_units, u + per);
+  if (u >= u_end) return;
+  walk_1x16<NT, DT, RECIPE, METRIC, PREC, GRAN, OUT, false>(args, tab, lane, u, u_end, 0.0f);
 }
 
 // ------------------------------------------------------------ 16x16 kernel
@@ -934,6 +942,171 @@ __global__ void k_band16(float* out, int64_t nbands) {
   }
 }
 
+// ------------------------------------------------------------ fused amax + quantize
+
+// One launch for the per-tensor amax and the quantize (the amax pre-pass the
+// Megatron-LM page runs as a separate torch reduction, "What does this PR
+// do?"). Phase 1: each wave takes the NaN-dropping max |x| over exactly the
+// unit range it quantizes later. A grid-wide max barrier combines the
+// workgroups' maxima. Phase 2: the 1x16 walk with the combined amax, over
+// data the wave just read (largely still in the Infinity Cache).
+//
+// The barrier is two-level so that same-address atomics stay few (they
+// serialize at the memory side): workgroup b arrives at group b % ng with
+// an atomic max and a count; the last arrival of a group forwards the group
+// max to the top level; the last top arrival publishes the amax and bumps
+// the generation word that every workgroup polls (each compares it with the
+// value it read before arriving, so the word never needs a reset). Each
+// level's counters and maxima are reset by its last arrival, so they are
+// zero again when the launch ends.
+//
+// The grid holds only as many workgroups as fit on the device at once, so
+// they all become resident unless other long-running work holds CUs (for
+// example a second fused launch on another stream). The poll is bounded
+// either way: after kSpinLimit polls a workgroup sets kStatusBarrier and
+// returns without quantizing rather than wait forever.
+
+// max |x| bits over blocks [b0, b1) of a flattened tensor: lane l takes
+// blocks b0 + l + 64 k, four in flight.
+template <int DT>
+__device__ __forceinline__ uint32_t range_absmax(const void* x, int64_t b0, int64_t b1, int lane) {
+  constexpr int kB = Raw<DT>::kBytes;
+  if (b1 <= b0) return 0u;
+  const Rsrc r = make_rsrc(static_cast<const char*>(x) + b0 * kB, (b1 - b0) * kB);
+  const uint32_t n = (uint32_t)(b1 - b0);
+  uint32_t m = 0;                  // fp32: magnitude bits
+  s16x2 k = pair_key<DT>(0u);      // 16-bit inputs: packed keys, starting at +0
+  for (uint32_t i = 0; i < n; i += 256) {
+    Raw<DT> q[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) q[j].load(r, (i + 64 * j + lane) * kB);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if constexpr (DT == kFP32) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const v4i v = q[j].v[t];
+          m = max(max(m, mag_bits(__int_as_float(v.x))), max(mag_bits(__int_as_float(v.y)),
+                  max(mag_bits(__int_as_float(v.z)), mag_bits(__int_as_float(v.w)))));
+        }
+      } else {
+        const uint32_t w[8] = {(uint32_t)q[j].a.x, (uint32_t)q[j].a.y, (uint32_t)q[j].a.z, (uint32_t)q[j].a.w,
+                               (uint32_t)q[j].b.x, (uint32_t)q[j].b.y, (uint32_t)q[j].b.z, (uint32_t)q[j].b.w};
+#pragma unroll
+        for (int t = 0; t < 8; t++) k = __builtin_elementwise_max(k, pair_key<DT>(w[t]));
+      }
+    }
+  }
+  if constexpr (DT == kFP32) return m;
+  else return pair_key_to_f32_bits<DT>(k);
+}
+
+constexpr int kBarGroups = 32;       // first-level arrival groups
+constexpr int kSpinLimit = 1 << 20;  // polls before giving up (each at least 128 cycles of sleep)
+
+// Word offsets in the workspace; every counter and maximum sits on a
+// 128-byte line of its own.
+struct BarWs {
+  uint32_t* w;
+  __device__ uint32_t* gen() const { return w; }
+  __device__ uint32_t* result() const { return w + 32; }
+  __device__ uint32_t* gcount(uint32_t g) const { return w + 64 + 32 * g; }
+  __device__ uint32_t* gmax(uint32_t g) const { return w + 64 + 32 * (kBarGroups + g); }
+  __device__ uint32_t* tcount() const { return w + 64 + 32 * (2 * kBarGroups); }
+  __device__ uint32_t* tmax() const { return w + 64 + 32 * (2 * kBarGroups + 1); }
+};
+static_assert((64 + 32 * (2 * kBarGroups + 2)) * 4 <= kFusedWorkspaceBytes, "workspace too small");
+
+// Wait until this wave's vector memory operations (atomics included) have
+// completed; also a compiler barrier for memory operations.
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Called by one thread per workgroup with the workgroup's max; returns false
+// when the poll limit was reached.
+//
+// Every value that crosses workgroups travels through an atomic read-modify-
+// write or an agent-scope atomic load or store (which the compiler issues
+// coherent across the XCDs' L2 caches); the order between two of them is
+// kept by waiting for the first to complete before issuing the second. No
+// acquire or release fence is used: at agent scope each one writes back or
+// invalidates the L2, which, issued by every workgroup, costs far more than
+// the barrier itself. Nothing else needs ordering: phase 2 reads only the
+// input, which the launch already sees.
+__device__ bool grid_max_barrier(const BarWs& ws, uint32_t m, uint32_t& result) {
+  constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
+  constexpr int kR = __ATOMIC_RELAXED;
+  const uint32_t G = gridDim.x;
+  const uint32_t ng = G < (uint32_t)kBarGroups ? G : (uint32_t)kBarGroups;
+  const uint32_t g = blockIdx.x % ng;
+  const uint32_t gsize = G / ng + (g < G % ng ? 1u : 0u);
+  const uint32_t g0 = __hip_atomic_load(ws.gen(), kR, kA);  // before arriving
+  vm_wait();
+  __hip_atomic_fetch_max(ws.gmax(g), m, kR, kA);
+  vm_wait();
+  if (__hip_atomic_fetch_add(ws.gcount(g), 1u, kR, kA) == gsize - 1) {
+    // last of its group: every member's max is in; forward it, reset the group
+    const uint32_t gm = __hip_atomic_exchange(ws.gmax(g), 0u, kR, kA);
+    __hip_atomic_store(ws.gcount(g), 0u, kR, kA);
+    __hip_atomic_fetch_max(ws.tmax(), gm, kR, kA);
+    vm_wait();
+    if (__hip_atomic_fetch_add(ws.tcount(), 1u, kR, kA) == ng - 1) {
+      const uint32_t a = __hip_atomic_exchange(ws.tmax(), 0u, kR, kA);
+      __hip_atomic_store(ws.tcount(), 0u, kR, kA);
+      __hip_atomic_store(ws.result(), a, kR, kA);
+      vm_wait();
+      __hip_atomic_fetch_add(ws.gen(), 1u, kR, kA);
+    }
+  }
+  for (int it = 0; __hip_atomic_load(ws.gen(), kR, kA) == g0; it++) {
+    if (it >= kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  result = __hip_atomic_load(ws.result(), kR, kA);
+  return true;
+}
+
+template <int DT, int RECIPE, int METRIC, int PREC>
+__global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t* workspace, float* amax_out) {
+  __shared__ float lds[4][256];
+  __shared__ uint32_t part[4];
+  __shared__ uint32_t amax_bits;
+  __shared__ int ok;
+  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
+  const int64_t u = min(args.total_units, wave * per);
+  const int64_t u_end = min(args.total_units, u + per);
+  const TensorRef& T = args.t[0];
+  const int64_t nblk = T.M * (T.K >> 4);
+
+  // phase 1
+  uint32_t m = range_absmax<DT>(T.x, min(nblk, u * kUB), min(nblk, u_end * kUB), lane);
+  m = wave_max_u32(m);
+  if (lane == 0) part[wv] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    ok = grid_max_barrier(BarWs{workspace}, max(max(part[0], part[1]), max(part[2], part[3])), a) ? 1 : 0;
+    amax_bits = a;
+    if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
+  }
+  __syncthreads();
+  if (!ok) return;
+  const float A = __uint_as_float(amax_bits);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (amax_out) amax_out[0] = A;
+    if (args.sdec_out) args.sdec_out[0] = 1.0f / global_encode_scale(A, args.six_b);
+  }
+
+  // phase 2
+  if (u >= u_end) return;
+  walk_1x16<1, DT, RECIPE, METRIC, PREC, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, A);
+}
+
 // ------------------------------------------------------------ dispatch
 
 // workgroups of 256 threads for an n-item elementwise helper (capped)
@@ -959,6 +1132,20 @@ static hipError_t launch_1x16_t(const Args1x16<NT>& a, hipStream_t s) {
   const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
+static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax_out, hipStream_t s) {
+  static_assert(GRAN == kGranTensor && OUT == kOutQuant, "fused: per-tensor quantize only");
+  auto* fn = &k_fused<DT, RECIPE, METRIC, PREC>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  Args1x16<1> args = a;
+  void* params[] = {&args, &ws, &amax_out};
+  // A plain launch: a cooperative one costs about 16 us more per call on
+  // this device. The grid holds only the workgroups that fit at once, so on
+  // a GPU without other long-running work all of them are resident.
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 
 template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
@@ -995,6 +1182,13 @@ hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran,
   if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, CALL_Q1) }
   if (gran == kGranRow) { FOS_DTYPES(kGranRow, kOutQuant, CALL_Q1) }
   FOS_DTYPES(kGranGroup, kOutQuant, CALL_Q1)
+}
+
+#define CALL_F(DT, R, M, P, G, O) launch_fused_t<DT, R, M, P, G, O>(a, ws, amax_out, s)
+
+hipError_t launch_fused(int dt, int recipe, int metric, int prec, const Args1x16<1>& a, uint32_t* ws,
+                        float* amax_out, hipStream_t s) {
+  FOS_DTYPES(kGranTensor, kOutQuant, CALL_F)
 }
 
 hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, hipStream_t s) {

@@ -141,3 +141,30 @@ def test_grouped_moe_65536x7168(orc):
         want_sdec = np.array([orc.global_decode_scale(float(a), bound) for a in gam], np.float32)
         np.testing.assert_array_equal(gsdec.cpu().numpy().view(np.uint32), want_sdec.view(np.uint32))
         assert int(status.item()) == 0
+
+
+def test_fused_dense_activation_8192x4096(orc):
+    """The fused amax + quantize on the full dense activation tensor, every
+    mode, with one workspace across calls of two sizes."""
+    M, K = 8192, 4096
+    x = synthdata.activation_family("outlier", M, K, 23, "bf16")
+    bits = raw_bits(x)
+    xd = x.to("cuda")
+    a = orc.amax(bits, "bf16", "tensor")
+    rows = sample_rows(M, 48, 23)
+    small = synthdata.normal(48, 1040, 5, "bf16")
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for (recipe, metric, prec), bound in itertools.product(MODES, BOUNDS):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+        codes, scales, amax, _ = fos.fos_quantize_fused(xd, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        want = orc.quantize(bits[rows], "bf16", a, **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"{kw}")
+        c2, s2, _, _ = fos.fos_quantize_fused(small.to("cuda"), workspace=ws, **kw)
+        torch.cuda.synchronize()
+        w2 = orc.quantize(raw_bits(small), "bf16", orc.amax(raw_bits(small), "bf16", "tensor"), **kw)
+        np.testing.assert_array_equal(c2.cpu().numpy(), w2["codes"])
+        np.testing.assert_array_equal(s2.cpu().numpy(), w2["scales"])
+    assert not ws[256:].any()

@@ -315,3 +315,54 @@ def test_runs_on_a_side_stream(orc):
     s.synchronize()
     np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
     np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+
+
+# ------------------------------------------------------------------ fused amax + quantize
+
+FUSED_CASES = [((67, 1552), "outlier"), ((256, 1024), "normal"), ((1, 16), "special"), ((96, 1040), "special"),
+               ((3, 4096), "uniform"), ((0, 64), "normal")]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_fused_amax_quantize(orc, dtype):
+    """One launch for the per-tensor amax and the quantize equals the oracle's
+    amax followed by its quantize, for every mode; the workspace comes back
+    counters zero after each call, so calls of different sizes can follow
+    each other."""
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for (M, K), family in FUSED_CASES:
+        x = _family(family, dtype, M, K, 61) if M else torch.empty(0, K, dtype=synthdata.TORCH_DTYPES[dtype])
+        b = raw_bits(x)
+        want_amax = orc.amax(b, dtype, "tensor")
+        for (recipe, metric, prec), bound in itertools.product(MODES, (448, 256)):
+            kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+            codes, scales, amax, sdec = fos.fos_quantize_fused(dev(x), workspace=ws, status=status, **kw)
+            torch.cuda.synchronize()
+            want = orc.quantize(b, dtype, want_amax, **kw)
+            np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), want_amax.view(np.uint32))
+            np.testing.assert_array_equal(sdec.cpu().numpy().view(np.uint32), want["sdec"].view(np.uint32))
+            np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{M}x{K} {kw}")
+            np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{M}x{K} {kw}")
+            assert not ws[256:].any(), "the workspace's counters must be zero after a call"
+    assert int(status.item()) == 0
+
+
+def test_fused_nan_inf_tensors(orc):
+    """NaN-dropping amax inside the fused launch: scattered NaN, an all-NaN
+    tensor (amax 0, S_enc 1) and an infinite element (S_enc 1)."""
+    base = synthdata.normal(64, 256, 62, "bf16").to(torch.float32)
+    cases = []
+    t = base.clone(); t[5, 7] = float("nan"); t[60, :] = float("nan"); cases.append(t)
+    cases.append(torch.full((32, 64), float("nan")))
+    t = base.clone(); t[10, 3] = float("inf"); cases.append(t)
+    for t in cases:
+        x = t.to(torch.bfloat16)
+        b = raw_bits(x)
+        a = orc.amax(b, "bf16", "tensor")
+        codes, scales, amax, sdec = fos.fos_quantize_fused(dev(x), recipe="4over6")
+        torch.cuda.synchronize()
+        want = orc.quantize(b, "bf16", a, recipe="4over6")
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
