@@ -27,6 +27,7 @@ BLOCKS = {"1x16": 0, "16x16": 1}
 GRANS = {"tensor": 0, "row": 1}
 METRICS = {"mae": 0, "mse": 1}
 PRECS = {"exact": 0, "fp16": 1}
+ORDERS = {"tree": 0, "seq": 1}
 AMAX_MODES = {"tensor": 0, "row": 1, "band16": 2}
 
 STATUS_TILE_NONUNIFORM = 1
@@ -52,7 +53,8 @@ def build(force: bool = True, out: str | None = None, src: str | None = None) ->
 class _Cfg(ctypes.Structure):
     _fields_ = [("recipe", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("scale_gran", ctypes.c_int32), ("err_metric", ctypes.c_int32),
-                ("err_prec", ctypes.c_int32), ("e4m3_bound", ctypes.c_int32)]
+                ("err_prec", ctypes.c_int32), ("e4m3_bound", ctypes.c_int32),
+                ("err_order", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -73,6 +75,7 @@ _SIGS = {
     "oracle_global_encode_scale": (ctypes.c_float, [ctypes.c_float, ctypes.c_int]),
     "oracle_global_decode_scale": (ctypes.c_float, [ctypes.c_float, ctypes.c_int]),
     "oracle_tree16": (ctypes.c_float, [_P]),
+    "oracle_seq16": (ctypes.c_float, [_P]),
     "oracle_amax": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_int, _P]),
     "oracle_quantize": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, ctypes.POINTER(_Cfg),
                                        _P, _P, _P, _P, _P, _P, _P]),
@@ -109,9 +112,9 @@ def _ptr(a):
 
 
 def _cfg(recipe="4over6", block="1x16", scale_gran="tensor", err_metric="mse", err_prec="exact",
-         bound=448) -> _Cfg:
+         bound=448, err_order="tree") -> _Cfg:
     return _Cfg(RECIPES[recipe], BLOCKS[block], GRANS[scale_gran], METRICS[err_metric],
-                PRECS[err_prec], int(bound))
+                PRECS[err_prec], int(bound), ORDERS[err_order])
 
 
 def _check_x(x, dtype):
@@ -164,6 +167,11 @@ class Oracle:
 
     def global_decode_scale(self, amax: float, bound: int) -> float:
         return self.lib.oracle_global_decode_scale(amax, bound)
+
+    def seq16(self, u) -> float:
+        u = np.ascontiguousarray(u, dtype=np.float32)
+        assert u.size == 16
+        return self.lib.oracle_seq16(_ptr(u))
 
     def tree16(self, u) -> float:
         u = np.ascontiguousarray(u, dtype=np.float32)

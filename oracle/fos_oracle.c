@@ -243,6 +243,16 @@ float oracle_tree16(const float* u) {
     return w[0];
 }
 
+/* Transformer Engine's sequential order, which the Megatron-LM PR keeps for
+ * its candidate errors ([MLM-QDQ] "What does this PR do?", FP16 error
+ * contract): the sixteen terms added left to right in element order,
+ * ((u0 + u1) + u2) + ... + u15, each + one binary32 addition. */
+float oracle_seq16(const float* u) {
+    float s = u[0];
+    for (int i = 1; i < 16; i++) s = s + u[i];
+    return s;
+}
+
 /* NaN-dropping max |x| with start value +0 ([AO-KERN]: NaN inputs take
  * NaN-dropping amaxes). |-0| = +0; an all-NaN set gives +0. */
 static float nan_dropping_absmax(float acc, float x) {
@@ -359,7 +369,7 @@ static void encode_candidate(const float* xb, int nrows, float a, float c, float
     out->err = 0.0f;
     if (want_err) {
         if (nrows == 1) {
-            out->err = oracle_tree16(terms);
+            out->err = (cfg->err_order == ORC_ORDER_SEQ) ? oracle_seq16(terms) : oracle_tree16(terms);
         } else {
             /* 16x16 tile: one pinned tree per row, then the same tree over
              * the sixteen row sums (row index order) */
@@ -427,6 +437,9 @@ static int cfg_ok(const orc_cfg* cfg) {
     if (cfg->err_metric != ORC_MAE && cfg->err_metric != ORC_MSE) return 0;
     if (cfg->err_prec != ORC_ERR_EXACT && cfg->err_prec != ORC_ERR_FP16) return 0;
     if (cfg->e4m3_bound != 448 && cfg->e4m3_bound != 256) return 0;
+    if (cfg->err_order != ORC_ORDER_TREE && cfg->err_order != ORC_ORDER_SEQ) return 0;
+    /* the sequential order is defined for 1x16 blocks only */
+    if (cfg->err_order == ORC_ORDER_SEQ && cfg->block != ORC_BLOCK_1X16) return 0;
     return 1;
 }
 

@@ -49,6 +49,11 @@ extern "C" {
 #define ORC_STATUS_TILE_NONUNIFORM 1
 #define ORC_STATUS_BAD_OFFS 2
 
+/* error-sum orders: the pinned width-16 tree, or a left-to-right sum over
+ * the block's sixteen terms (1x16 blocks only) */
+#define ORC_ORDER_TREE 0
+#define ORC_ORDER_SEQ 1
+
 typedef struct orc_cfg {
     int32_t recipe;
     int32_t block;
@@ -56,6 +61,7 @@ typedef struct orc_cfg {
     int32_t err_metric;
     int32_t err_prec;
     int32_t e4m3_bound; /* 448 or 256 */
+    int32_t err_order;  /* ORC_ORDER_TREE or ORC_ORDER_SEQ */
 } orc_cfg;
 
 /* element formats */
@@ -80,6 +86,7 @@ float oracle_global_decode_scale(float amax, int e4m3_bound);
 
 /* T16 reduction of 16 terms in the pinned order */
 float oracle_tree16(const float* u);
+float oracle_seq16(const float* u);
 
 int oracle_amax(const void* x, int dtype, int64_t M, int64_t K, int mode, float* out);
 

@@ -6,7 +6,8 @@ even, E4M3 block scales are found by searching all 127 finite non-negative
 codes (decoded by torch's float8_e4m3fn), E2M1 codes by searching the eight
 OCP grid magnitudes, and binary16 rounding uses numpy's float16 cast. The
 error sum follows a lane-by-lane model of a clamped shuffle-down over sixteen
-lanes. It is slow and meant for a handful of blocks.
+lanes, or (the sequential order) a left-to-right sum. It is slow and meant
+for a handful of blocks.
 """
 from __future__ import annotations
 
@@ -95,6 +96,14 @@ def lane_tree(terms):
     return lanes[0]
 
 
+def left_fold(terms):
+    """Left-to-right sum in element order, each addition rounded."""
+    s = terms[0]
+    for t in terms[1:]:
+        s = add(s, t)
+    return s
+
+
 def nearest_e4m3(t: float) -> int:
     if t >= 448.0:
         return 0x7E
@@ -133,7 +142,7 @@ def global_scales(A: float, bound: int):
     return s, div(1.0, s)
 
 
-def quantize_block(xs, nrows: int, A: float, bound: int, recipe: str, metric: str, prec: str):
+def quantize_block(xs, nrows: int, A: float, bound: int, recipe: str, metric: str, prec: str, order: str = "tree"):
     """xs: 16 * nrows binary32 values (row-major). Returns (codes, scale, kept, err6, err4)."""
     S_enc, S_dec = global_scales(A, bound)
     a = 0.0
@@ -158,7 +167,7 @@ def quantize_block(xs, nrows: int, A: float, bound: int, recipe: str, metric: st
             e = sub(x, ref)
             terms.append(abs(e) if metric == "mae" else mul(e, e))
         if nrows == 1:
-            err = lane_tree(terms)
+            err = left_fold(terms) if order == "seq" else lane_tree(terms)
         else:
             err = lane_tree([lane_tree(terms[16 * r:16 * r + 16]) for r in range(16)])
         results[c] = (codes, k, err)
@@ -175,7 +184,7 @@ def quantize_block(xs, nrows: int, A: float, bound: int, recipe: str, metric: st
 
 
 def quantize_tensor(x: np.ndarray, amax: np.ndarray, block: str, scale_gran: str, bound: int, recipe: str,
-                    metric: str, prec: str):
+                    metric: str, prec: str, order: str = "tree"):
     """x: float64 array [M, K] of binary32 values. Returns codes [M, K/2],
     scales [M, K/16], kept [nblocks], errs [nblocks, 2]."""
     M, K = x.shape
@@ -188,7 +197,7 @@ def quantize_tensor(x: np.ndarray, amax: np.ndarray, block: str, scale_gran: str
         A = float(amax[0] if scale_gran == "tensor" else amax[r0])
         for cb in range(K // 16):
             xs = [float(v) for v in x[r0:r0 + nrows, cb * 16:cb * 16 + 16].reshape(-1)]
-            q, k, kept, e6, e4 = quantize_block(xs, nrows, A, bound, recipe, metric, prec)
+            q, k, kept, e6, e4 = quantize_block(xs, nrows, A, bound, recipe, metric, prec, order)
             kept_l.append(kept)
             errs.append((e6, e4))
             for i in range(nrows):

@@ -71,6 +71,45 @@ def test_oracle_matches_exact_model(orc, dtype, family, block, gran, bound):
             np.testing.assert_array_equal(got["err"].astype(np.float64), errs)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("family", ["normal", "outlier", "special", "weight"])
+@pytest.mark.parametrize("gran", ["tensor", "row"])
+def test_sequential_order_matches_exact_model(orc, dtype, family, gran):
+    """The sequential error order (1x16) against the exact model's left fold,
+    every mode and bound."""
+    M, K = 3, 48
+    seed = zlib.crc32(repr(("seq", dtype, family, gran)).encode()) % 1000
+    t = _data(family, dtype, M, K, seed)
+    bits = raw_bits(t)
+    xv = _values(t)
+    for bound in (448, 256):
+        amax = _amax(orc, t, dtype, gran, "1x16", 1.0 if bound == 448 else 1.0 / 3.0)
+        for recipe, metric, prec in MODES:
+            got = orc.quantize(bits, dtype, amax, debug=True, recipe=recipe, scale_gran=gran, err_metric=metric,
+                               err_prec=prec, bound=bound, err_order="seq")
+            codes, scales, kept, errs = exact_model.quantize_tensor(xv, amax, "1x16", gran, bound, recipe, metric,
+                                                                    prec, order="seq")
+            np.testing.assert_array_equal(got["codes"], codes, err_msg=f"{recipe} {metric} {prec}")
+            np.testing.assert_array_equal(got["scales"], scales)
+            np.testing.assert_array_equal(got["choice"], kept)
+            if recipe == "4over6":
+                np.testing.assert_array_equal(got["err"].astype(np.float64), errs)
+
+
+def test_sequential_order_changes_some_choices(orc):
+    """On the outlier family the two orders disagree on some candidate errors,
+    so the knob is exercised; 16x16 blocks reject the sequential order."""
+    t = synthdata.activation_family("outlier", 64, 512, 9, "bf16")
+    bits = raw_bits(t)
+    a = orc.amax(bits, "bf16", "tensor")
+    kw = dict(recipe="4over6", err_metric="mse", err_prec="exact")
+    tr = orc.quantize(bits, "bf16", a, debug=True, err_order="tree", **kw)
+    sq = orc.quantize(bits, "bf16", a, debug=True, err_order="seq", **kw)
+    assert not np.array_equal(tr["err"], sq["err"])
+    with pytest.raises(ValueError):
+        orc.quantize(raw_bits(synthdata.weight(16, 32, 1, "bf16")), "bf16", a, block="16x16", err_order="seq")
+
+
 @pytest.mark.parametrize("metric,prec", [("mse", "fp16"), ("mae", "fp16")])
 def test_fp16_error_mode_exercised(orc, metric, prec):
     """On weights with a non-dyadic global scale the binary16 rounding of the

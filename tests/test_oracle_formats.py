@@ -217,6 +217,25 @@ def test_tree16_exact_value(orc):
     assert seq == np.float32(1.0)
 
 
+def test_seq16_exact_values(orc):
+    """The sequential order in closed form: one 1.0 then fifteen 2^-24 stays
+    1.0 (each addition is a tie that rounds back to the even 1.0); the same
+    terms reversed sum exactly to 15 * 2^-24 first, and 1 + 7.5 ulp rounds to
+    the even 1 + 8 ulp = 1 + 2^-20."""
+    u = np.array([1.0] + [2.0 ** -24] * 15, np.float32)
+    assert orc.seq16(u) == np.float32(1.0)
+    assert orc.seq16(u[::-1].copy()) == np.float32(1.0 + 2.0 ** -20)
+    # all terms equal to 2^-3: every partial sum is exact
+    assert orc.seq16(np.full(16, 0.125, np.float32)) == np.float32(2.0)
+    # 2^24 then fifteen ones: sequentially each 2^24 + 1 is a tie that stays
+    # at the even 2^24. The tree: stride 8 gives lane 0 2^24 + 1 -> 2^24 and
+    # lanes 1..7 the value 2; stride 4: 2^24 + 2, 4, 4, 4; stride 2:
+    # 2^24 + 6, 8; stride 1: 2^24 + 14 (all exact past the first tie).
+    v = np.array([2.0 ** 24] + [1.0] * 15, np.float32)
+    assert orc.seq16(v) == np.float32(2.0 ** 24)
+    assert orc.tree16(v) == np.float32(2.0 ** 24 + 14.0)
+
+
 def test_tree16_matches_shuffle_down_model(orc):
     rng = np.random.default_rng(5)
     for _ in range(3000):
