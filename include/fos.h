@@ -41,8 +41,9 @@
  *    block and global amaxes drop NaN, and a NaN element encodes to +6.
  *  - Every result is bitwise defined: one binary32 operation per step,
  *    round-to-nearest-even, E4M3/E2M1 casts RNE with saturation, the error
- *    terms of a block summed by the pinned shuffle-down tree (strides 8, 4, 2,
- *    1), the map-to-4 candidate kept only on a strictly lower error.
+ *    terms of a block summed in one pinned order (the shuffle-down tree with
+ *    strides 8, 4, 2, 1 by default, or a left-to-right sum), the map-to-4
+ *    candidate kept only on a strictly lower error.
  */
 #ifndef FOS_H
 #define FOS_H
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FOS_ABI_VERSION 1
+#define FOS_ABI_VERSION 2
 
 /* element types */
 #define FOS_BF16 0
@@ -80,6 +81,15 @@ extern "C" {
  * value, or against that value rounded to binary16 */
 #define FOS_ERR_EXACT 0
 #define FOS_ERR_FP16 1
+
+/* fos_config.err_order (four-over-six only): the order in which a block's
+ * sixteen error terms are summed. The tree is the width-16 shuffle-down order
+ * the kernel page pins (wolfcomos/ao PR, description); the sequential order,
+ * ((u0 + u1) + u2) + ... + u15, is Transformer Engine's term order that the
+ * Megatron-LM PR keeps ("What does this PR do?", FP16 error contract). The
+ * sequential order is defined for 1x16 blocks only. */
+#define FOS_ORDER_TREE 0
+#define FOS_ORDER_SEQ 1
 
 /* fos_amax granularity */
 #define FOS_AMAX_TENSOR 0
@@ -111,13 +121,14 @@ typedef struct fos_config {
     int32_t err_metric; /* FOS_ERR_MAE | FOS_ERR_MSE */
     int32_t err_prec;   /* FOS_ERR_EXACT | FOS_ERR_FP16 */
     int32_t e4m3_bound; /* 448 or 256 */
+    int32_t err_order;  /* FOS_ORDER_TREE | FOS_ORDER_SEQ (added in ABI version 2) */
 } fos_config;
 
 /* One tensor of a weight list (fos_qdq_list). */
 typedef struct fos_tensor_desc {
     const void* x;      /* [M, K] input */
     void* y;            /* [M, K] output, same element type */
-    const float* amax;  /* device FP32 per-tensor amax, [1] */
+    const float* amax;  /* device FP32 amax: [1] per tensor, or [M] per row */
     int64_t M;
     int64_t K;
 } fos_tensor_desc;
@@ -147,17 +158,21 @@ int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* am
                  uint8_t* codes, uint8_t* scales, float* sdec_out, int32_t* d_status, void* stream);
 
 /* Fused fake quantization: y[M, K] = the kept candidate's decoded values,
- * rounded once to the input type (bf16 or fp16, RNE); no codes or scales are
- * written (Megatron-LM PR, "What does this PR do?": fused data path, caller-
- * provided FP32 per-tensor amax, 1x16 blocks). Bitwise equal to
- * nvfp4_dequantize(fos_quantize(x)). The config must be 1x16 per-tensor. */
+ * rounded once to the input type (RNE); no codes or scales are written
+ * (Megatron-LM PR, "What does this PR do?": fused data path with a caller-
+ * provided FP32 per-tensor amax, 1x16 blocks, bf16/fp16). Bitwise equal to
+ * nvfp4_dequantize(fos_quantize(x)) for every config fos_quantize takes:
+ * bf16, fp16 or fp32; 1x16 or 16x16 blocks; amax per tensor [1] or per row
+ * [M] (16x16: equal within each 16-row band). */
 int fos_qdq(const void* x, int dtype, int64_t M, int64_t K, const float* amax, const fos_config* cfg, void* y,
             void* stream);
 
 /* fos_qdq over a list of n independently stored rank-2 tensors of one
- * element type, in one launch per 64 tensors (the list API of the Megatron-LM
- * PR maps any number of discrete weights). `descs` is a HOST array; it is
- * copied into the launch arguments, so the caller may reuse it on return. */
+ * element type (the list API of the Megatron-LM PR maps any number of
+ * discrete weights): 1x16 blocks take one launch per 48 tensors, 16x16 tiles
+ * one launch per tensor. Each descriptor's amax is [1] (per tensor) or [M]
+ * (per row). `descs` is a HOST array; it is copied into the launch
+ * arguments, so the caller may reuse it on return. */
 int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_config* cfg, void* stream);
 
 /* Standard NVFP4 decode, recipe-agnostic (pytorch/ao PR, recipe commit:

@@ -24,6 +24,7 @@ BLOCKS = {"1x16": 0, "16x16": 1}
 GRANS = {"tensor": 0, "row": 1}
 METRICS = {"mae": 0, "mse": 1}
 PRECS = {"exact": 0, "fp16": 1}
+ORDERS = {"tree": 0, "seq": 1}
 AMAX_GRANS = {"tensor": 0, "row": 1, "band16": 2}
 
 STATUS_TILE_NONUNIFORM = 1
@@ -40,7 +41,8 @@ class FosError(RuntimeError):
 
 class _Config(ctypes.Structure):
     _fields_ = [("recipe", ctypes.c_int32), ("block", ctypes.c_int32), ("scale_gran", ctypes.c_int32),
-                ("err_metric", ctypes.c_int32), ("err_prec", ctypes.c_int32), ("e4m3_bound", ctypes.c_int32)]
+                ("err_metric", ctypes.c_int32), ("err_prec", ctypes.c_int32), ("e4m3_bound", ctypes.c_int32),
+                ("err_order", ctypes.c_int32)]
 
 
 class _Desc(ctypes.Structure):
@@ -93,9 +95,9 @@ def _check(rc: int):
 
 
 def config(recipe="4over6", block="1x16", scale_gran="tensor", err_metric="mse", err_prec="exact",
-           bound=448) -> _Config:
+           bound=448, err_order="tree") -> _Config:
     return _Config(RECIPES[recipe], BLOCKS[block], GRANS[scale_gran], METRICS[err_metric], PRECS[err_prec],
-                   int(bound))
+                   int(bound), ORDERS[err_order])
 
 
 def _ptr(t):

@@ -82,6 +82,10 @@ int check_cfg(const fos_config* c) {
     return fail(FOS_ERR_INVALID_ARG, "bad err_metric %d", c->err_metric);
   if (c->err_prec != FOS_ERR_EXACT && c->err_prec != FOS_ERR_FP16) return fail(FOS_ERR_INVALID_ARG, "bad err_prec %d", c->err_prec);
   if (c->e4m3_bound != 448 && c->e4m3_bound != 256) return fail(FOS_ERR_CONFIG, "e4m3_bound must be 448 or 256, got %d", c->e4m3_bound);
+  if (c->err_order != FOS_ORDER_TREE && c->err_order != FOS_ORDER_SEQ)
+    return fail(FOS_ERR_INVALID_ARG, "bad err_order %d", c->err_order);
+  if (c->err_order == FOS_ORDER_SEQ && c->block != FOS_BLOCK_1X16 && c->recipe == FOS_RECIPE_4OVER6)
+    return fail(FOS_ERR_CONFIG, "the sequential error order is defined for 1x16 blocks only");
   return FOS_OK;
 }
 
@@ -100,9 +104,11 @@ float six_b(const fos_config* c) { return 6.0f * (float)c->e4m3_bound; }
 
 // the error knobs are ignored by the standard recipe: normalize them so the
 // dispatch picks its one instance
-void mode_of(const fos_config* c, int& metric, int& prec) {
-  metric = c->recipe == FOS_RECIPE_NVFP4 ? FOS_ERR_MSE : c->err_metric;
-  prec = c->recipe == FOS_RECIPE_NVFP4 ? FOS_ERR_EXACT : c->err_prec;
+void mode_of(const fos_config* c, int& metric, int& prec, int& order) {
+  const bool std = c->recipe == FOS_RECIPE_NVFP4;
+  metric = std ? FOS_ERR_MSE : c->err_metric;
+  prec = std ? FOS_ERR_EXACT : c->err_prec;
+  order = std ? FOS_ORDER_TREE : c->err_order;
 }
 
 }  // namespace
@@ -165,8 +171,8 @@ int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* am
   if (!aligned(amax, 4) || !aligned(sdec_out, 4) || !aligned(d_status, 4)) return fail(FOS_ERR_ALIGN, "amax/sdec/status misaligned");
   if ((rc = check_device())) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int metric, prec;
-  mode_of(cfg, metric, prec);
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
   const bool per_row = cfg->scale_gran == FOS_PER_ROW;
   // the kernels also write S_dec; with no elements only S_dec remains
   if (M * K == 0 && !(sdec_out && (per_row ? M : 1) > 0)) return FOS_OK;
@@ -183,7 +189,7 @@ int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* am
     a.codes = codes;
     a.scales = scales;
     a.sdec_out = sdec_out;
-    return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec,
+    return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, order,
                                                 per_row ? fos::kGranRow : fos::kGranTensor, a, s));
   }
   fos::Args16x16 a;
@@ -197,28 +203,19 @@ int fos_quantize(const void* x, int dtype, int64_t M, int64_t K, const float* am
   a.scales = scales;
   a.sdec_out = sdec_out;
   a.status = d_status;
-  return launch_status(fos::launch_quant_16x16(dtype, cfg->recipe, metric, prec,
-                                               per_row ? fos::kGranRow : fos::kGranTensor, a, s));
-}
-
-static int check_qdq_cfg(const fos_config* cfg, int dtype) {
-  int rc;
-  if ((rc = check_cfg(cfg))) return rc;
-  if (dtype != FOS_BF16 && dtype != FOS_FP16) return fail(FOS_ERR_DTYPE, "fused QDQ takes bf16 or fp16, got dtype %d", dtype);
-  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
-    return fail(FOS_ERR_CONFIG, "fused QDQ supports 1x16 blocks with a per-tensor amax");
-  return FOS_OK;
+  return launch_status(fos::launch_16x16(dtype, cfg->recipe, metric, prec,
+                                         per_row ? fos::kGranRow : fos::kGranTensor, fos::kOutQuant, a, s));
 }
 
 int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_config* cfg, void* stream) {
   int rc;
   if ((rc = check_dtype(dtype))) return rc;
-  if ((rc = check_qdq_cfg(cfg, dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
   if (n < 0) return fail(FOS_ERR_INVALID_ARG, "n < 0");
   if (n > 0 && !descs) return fail(FOS_ERR_INVALID_ARG, "descs is NULL");
   for (int i = 0; i < n; i++) {
     const fos_tensor_desc& d = descs[i];
-    if ((rc = check_shape(d.M, d.K, FOS_BLOCK_1X16))) return fail(rc, "tensor %d: %s", i, g_last_error.c_str());
+    if ((rc = check_shape(d.M, d.K, cfg->block))) return fail(rc, "tensor %d: %s", i, g_last_error.c_str());
     if (!d.amax) return fail(FOS_ERR_INVALID_ARG, "tensor %d: amax is NULL", i);
     if (d.M * d.K > 0 && (!d.x || !d.y)) return fail(FOS_ERR_INVALID_ARG, "tensor %d: x/y is NULL", i);
     if (!aligned(d.x, 16) || !aligned(d.y, 16)) return fail(FOS_ERR_ALIGN, "tensor %d: x/y not 16-byte aligned", i);
@@ -226,8 +223,29 @@ int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_confi
   }
   if ((rc = check_device())) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int metric, prec;
-  mode_of(cfg, metric, prec);
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
+  const bool per_row = cfg->scale_gran == FOS_PER_ROW;
+  const int gran = per_row ? fos::kGranRow : fos::kGranTensor;
+  if (cfg->block == FOS_BLOCK_16X16) {
+    // one 16x16 launch per tensor
+    for (int i = 0; i < n; i++) {
+      const fos_tensor_desc& d = descs[i];
+      if (d.M * d.K == 0) continue;
+      fos::Args16x16 a;
+      memset(&a, 0, sizeof a);
+      a.x = d.x;
+      a.y = d.y;
+      a.amax = d.amax;
+      a.M = d.M;
+      a.K = d.K;
+      a.six_b = six_b(cfg);
+      if ((rc = launch_status(fos::launch_16x16(dtype, cfg->recipe, metric, prec, gran, fos::kOutQdq, a, s))))
+        return rc;
+    }
+    return FOS_OK;
+  }
+  const int64_t ub = fos::unit_blocks(fos::kOutQdq, dtype);
   int i = 0;
   while (i < n) {
     fos::Args1x16<fos::kMaxList> a;
@@ -237,12 +255,13 @@ int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_confi
       const fos_tensor_desc& d = descs[i];
       if (d.M * d.K == 0) continue;
       a.t[a.n++] = fos::TensorRef{d.x, d.y, d.amax, d.M, d.K, units};
-      units += (d.M * (d.K / 16) + fos::unit_blocks(fos::kOutQdq, dtype) - 1) / fos::unit_blocks(fos::kOutQdq, dtype);
+      // units: 64 blocks of the flattened tensor, or per-row segments
+      units += per_row ? d.M * ((d.K / 16 + ub - 1) / ub) : (d.M * (d.K / 16) + ub - 1) / ub;
     }
     if (a.n == 0) continue;
     a.total_units = units;
     a.six_b = six_b(cfg);
-    if ((rc = launch_status(fos::launch_qdq_1x16(dtype, cfg->recipe, metric, prec, a, s)))) return rc;
+    if ((rc = launch_status(fos::launch_qdq_1x16(dtype, cfg->recipe, metric, prec, order, gran, a, s)))) return rc;
   }
   return FOS_OK;
 }
@@ -285,8 +304,8 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
     return fail(FOS_ERR_ALIGN, "offs/amax/sdec/status misaligned");
   if ((rc = check_device())) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int metric, prec;
-  mode_of(cfg, metric, prec);
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
   fos::Args1x16<1> a;
   memset(&a, 0, sizeof a);
   a.t[0] = fos::TensorRef{x, nullptr, nullptr, M_alloc, K > 0 ? K : 16, 0};
@@ -301,7 +320,7 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
   a.status = d_status;
   a.offs = offs;
   a.group_amax = group_amax;
-  return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, fos::kGranGroup, a, s));
+  return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, order, fos::kGranGroup, a, s));
 }
 
 int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
@@ -319,8 +338,8 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   if (!aligned(workspace, 4) || !aligned(amax_out, 4) || !aligned(sdec_out, 4) || !aligned(d_status, 4))
     return fail(FOS_ERR_ALIGN, "workspace/amax/sdec/status misaligned");
   if ((rc = check_device())) return rc;
-  int metric, prec;
-  mode_of(cfg, metric, prec);
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
   fos::Args1x16<1> a;
   memset(&a, 0, sizeof a);
   a.t[0] = fos::TensorRef{x, nullptr, nullptr, M, K > 0 ? K : 16, 0};
@@ -332,7 +351,7 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   a.scales = scales;
   a.sdec_out = sdec_out;
   a.status = d_status;
-  return launch_status(fos::launch_fused(dtype, cfg->recipe, metric, prec, a, static_cast<uint32_t*>(workspace),
+  return launch_status(fos::launch_fused(dtype, cfg->recipe, metric, prec, order, a, static_cast<uint32_t*>(workspace),
                                          amax_out, static_cast<hipStream_t>(stream)));
 }
 

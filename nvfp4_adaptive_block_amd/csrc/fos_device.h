@@ -162,6 +162,15 @@ __device__ __forceinline__ float dpp(float v) {
 }
 constexpr int kDppRowShl = 0x100, kDppRowRor = 0x120, kDppRowBcast = 0x150;
 
+// The sequential order: the sixteen terms added left to right in element
+// order (Transformer Engine's order, kept by the Megatron-LM page).
+__device__ __forceinline__ float seq16(const float* u) {
+  float s = u[0];
+#pragma unroll
+  for (int i = 1; i < 16; i++) s = s + u[i];
+  return s;
+}
+
 // The same tree across the 16 lanes of a DPP row (lanes 16k .. 16k+15 hold
 // terms 0..15): at each stride s (8, 4, 2, 1) lane i adds lane i + s, so
 // lane 16k ends with the pinned sum; the result is then broadcast to all 16

@@ -12,6 +12,7 @@ enum { kBF16 = 0, kFP16 = 1, kFP32 = 2 };
 enum { kNVFP4 = 0, k4over6 = 1 };
 enum { kMAE = 0, kMSE = 1 };
 enum { kErrExact = 0, kErrFP16 = 1 };
+enum { kOrderTree = 0, kOrderSeq = 1 };
 enum { kGranTensor = 0, kGranRow = 1, kGranGroup = 2 };
 enum { kOutQuant = 0, kOutQdq = 1 };
 enum { kAmaxTensor = 0, kAmaxRow = 1, kAmaxBand16 = 2 };
@@ -78,12 +79,14 @@ struct Args16x16 {
   int32_t* status;
 };
 
-hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a,
+hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int order, int gran, const Args1x16<1>& a,
                              hipStream_t s);
-hipError_t launch_fused(int dt, int recipe, int metric, int prec, const Args1x16<1>& a, uint32_t* ws,
+hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                         float* amax_out, hipStream_t s);
-hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, hipStream_t s);
-hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, hipStream_t s);
+hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, int gran,
+                           const Args1x16<kMaxList>& a, hipStream_t s);
+hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int out, const Args16x16& a,
+                        hipStream_t s);
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,
                           int64_t M, int64_t K, void* y, int grid, hipStream_t s);
 hipError_t launch_amax(int dt, int gran, const void* x, int64_t M, int64_t K, float* out, int grid, hipStream_t s);

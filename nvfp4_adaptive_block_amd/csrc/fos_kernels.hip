@@ -266,8 +266,9 @@ __device__ __forceinline__ void decode16(uint32_t c0, uint32_t c1, float D, floa
   for (int i = 0; i < 16; i++) xh[i] = q[i] * D;
 }
 
-// Error terms of one row segment (16 elements) and their pinned tree sum.
-template <int METRIC, int PREC>
+// Error terms of one row segment (16 elements) and their sum in the pinned
+// order (the tree, or the sequential order for 1x16 blocks).
+template <int METRIC, int PREC, int ORDER>
 __device__ __forceinline__ float err16(const float* x, const float* xh) {
   float u[16];
 #pragma unroll
@@ -275,7 +276,7 @@ __device__ __forceinline__ float err16(const float* x, const float* xh) {
     const float e = (PREC == kErrFP16) ? sub_f16(x[i], xh[i]) : x[i] - xh[i];
     u[i] = (METRIC == kMAE) ? __builtin_fabsf(e) : e * e;
   }
-  return tree16(u);
+  return ORDER == kOrderSeq ? seq16(u) : tree16(u);
 }
 
 struct BlockOut {
@@ -286,7 +287,7 @@ struct BlockOut {
 // Quantize one 1x16 block held in x. When NEED_XHAT, xh receives the kept
 // candidate's decoded values. Returns false when the fast form cannot be
 // trusted (the block holds a NaN); the caller then reruns with CAREFUL.
-template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, bool TAB>
+template <int RECIPE, int METRIC, int PREC, int ORDER, bool CAREFUL, bool NEED_XHAT, bool TAB>
 __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_dec, const Table& tab, BlockOut& o,
                                            float* xh) {
   const float a = amax16<CAREFUL>(x);
@@ -302,7 +303,7 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
     {
       float t[16];
       decode16(c60, c61, k6.D, t);
-      e6 = err16<METRIC, PREC>(x, t);
+      e6 = err16<METRIC, PREC, ORDER>(x, t);
     }
     __builtin_amdgcn_sched_barrier(0);
     const Cand k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
@@ -312,7 +313,7 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
     {
       float t[16];
       decode16(c40, c41, k4.D, t);
-      e4 = err16<METRIC, PREC>(x, t);
+      e4 = err16<METRIC, PREC, ORDER>(x, t);
     }
     __builtin_amdgcn_sched_barrier(0);
     const bool four = e4 < e6;
@@ -351,7 +352,7 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
       {
         float t[16];
         decode16(c60, c61, k6.D, t);
-        e6 = tree16_lanes(err16<METRIC, PREC>(x, t));
+        e6 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, t));
       }
       __builtin_amdgcn_sched_barrier(0);
       k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
@@ -359,7 +360,7 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
       {
         float t[16];
         decode16(c40, c41, k4.D, t);
-        e4 = tree16_lanes(err16<METRIC, PREC>(x, t));
+        e4 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, t));
       }
       __builtin_amdgcn_sched_barrier(0);
     } else {
@@ -370,8 +371,8 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
       float xh6[16], xh4[16];
       decode16(c60, c61, k6.D, xh6);
       decode16(c40, c41, k4.D, xh4);
-      e6 = tree16_lanes(err16<METRIC, PREC>(x, xh6));
-      e4 = tree16_lanes(err16<METRIC, PREC>(x, xh4));
+      e6 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, xh6));
+      e4 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, xh4));
     }
     const bool four = e4 < e6;
     o.c0 = four ? c40 : c60;
@@ -384,11 +385,11 @@ __device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_
 
 // Quantize a 1x16 block with the fast form, falling back to the careful form
 // when the block holds a NaN.
-template <int RECIPE, int METRIC, int PREC, bool NEED_XHAT, bool TAB>
+template <int RECIPE, int METRIC, int PREC, int ORDER, bool NEED_XHAT, bool TAB>
 __device__ __forceinline__ void quantize_block(const float* x, float S_enc, float S_dec, const Table& tab,
                                                BlockOut& o, float* xh) {
-  if (!block_1x16<RECIPE, METRIC, PREC, false, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh))
-    block_1x16<RECIPE, METRIC, PREC, true, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh);
+  if (!block_1x16<RECIPE, METRIC, PREC, ORDER, false, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh))
+    block_1x16<RECIPE, METRIC, PREC, ORDER, true, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh);
 }
 
 // ------------------------------------------------------------ 1x16 kernel
@@ -499,7 +500,7 @@ struct Walk {
 // The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED (per-
 // tensor scale only) the global amax is `fused_amax` rather than the
 // tensor's amax in memory.
-template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT, bool FUSED>
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT, bool FUSED>
 __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
                                           int64_t u_end, float fused_amax) {
   constexpr bool kXhat = OUT == kOutQdq;
@@ -564,7 +565,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
         float x[16], xh[16];
         raw[j].unpack(x);
         BlockOut o;
-        quantize_block<RECIPE, METRIC, PREC, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
+        quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
         if (OUT == kOutQuant) {
           store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
           store_scale(U.scl, off_s + j * 64, o.scale);
@@ -609,7 +610,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
   }
 }
 
-template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
   __shared__ float lds[4][256];
   const int lane = threadIdx.x & 63;
@@ -624,7 +625,7 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
   const int64_t u = wave * per;
   const int64_t u_end = min(args.total_units, u + per);
   if (u >= u_end) return;
-  walk_1x16<NT, DT, RECIPE, METRIC, PREC, GRAN, OUT, false>(args, tab, lane, u, u_end, 0.0f);
+  walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, 0.0f);
 }
 
 // ------------------------------------------------------------ 16x16 kernel
@@ -1065,7 +1066,7 @@ __device__ bool grid_max_barrier(const BarWs& ws, uint32_t m, uint32_t& result) 
   return true;
 }
 
-template <int DT, int RECIPE, int METRIC, int PREC>
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
 __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t* workspace, float* amax_out) {
   __shared__ float lds[4][256];
   __shared__ uint32_t part[4];
@@ -1104,7 +1105,7 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
 
   // phase 2
   if (u >= u_end) return;
-  walk_1x16<1, DT, RECIPE, METRIC, PREC, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, A);
+  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, A);
 }
 
 // ------------------------------------------------------------ dispatch
@@ -1125,19 +1126,19 @@ static int64_t resident_grid(const void* fn) {
   return (int64_t)cus * per_cu;
 }
 
-template <int NT, int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
 static hipError_t launch_1x16_t(const Args1x16<NT>& a, hipStream_t s) {
-  auto* fn = &k_1x16<NT, DT, RECIPE, METRIC, PREC, GRAN, OUT>;
+  auto* fn = &k_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
   const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
 static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax_out, hipStream_t s) {
   static_assert(GRAN == kGranTensor && OUT == kOutQuant, "fused: per-tensor quantize only");
-  auto* fn = &k_fused<DT, RECIPE, METRIC, PREC>;
+  auto* fn = &k_fused<DT, RECIPE, METRIC, PREC, ORDER>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
   const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
   Args1x16<1> args = a;
@@ -1160,45 +1161,65 @@ static hipError_t launch_16x16_t(const Args16x16& a, hipStream_t s) {
 }
 
 // Expand the runtime knobs into template instances. Every mode is a compiled
-// specialization; the kernels never branch on a mode.
-#define FOS_MODES(DT, GRAN, OUT, CALL)                                                          \
+// specialization; the kernels never branch on a mode. FOS_MODES covers the
+// 1x16 kernels (with the error order), FOS_MODES_T the 16x16 kernel (tree
+// order only).
+#define FOS_MODES(DT, GRAN, OUT, CALL)                                                                      \
+  if (recipe == kNVFP4) return CALL(DT, kNVFP4, kMSE, kErrExact, kOrderTree, GRAN, OUT);                     \
+  if (order == kOrderSeq) {                                                                                  \
+    if (metric == kMAE && prec == kErrExact) return CALL(DT, k4over6, kMAE, kErrExact, kOrderSeq, GRAN, OUT); \
+    if (metric == kMAE && prec == kErrFP16) return CALL(DT, k4over6, kMAE, kErrFP16, kOrderSeq, GRAN, OUT);   \
+    if (metric == kMSE && prec == kErrExact) return CALL(DT, k4over6, kMSE, kErrExact, kOrderSeq, GRAN, OUT); \
+    return CALL(DT, k4over6, kMSE, kErrFP16, kOrderSeq, GRAN, OUT);                                          \
+  }                                                                                                          \
+  if (metric == kMAE && prec == kErrExact) return CALL(DT, k4over6, kMAE, kErrExact, kOrderTree, GRAN, OUT);  \
+  if (metric == kMAE && prec == kErrFP16) return CALL(DT, k4over6, kMAE, kErrFP16, kOrderTree, GRAN, OUT);    \
+  if (metric == kMSE && prec == kErrExact) return CALL(DT, k4over6, kMSE, kErrExact, kOrderTree, GRAN, OUT);  \
+  return CALL(DT, k4over6, kMSE, kErrFP16, kOrderTree, GRAN, OUT);
+
+#define FOS_MODES_T(DT, GRAN, OUT, CALL)                                                          \
   if (recipe == kNVFP4) return CALL(DT, kNVFP4, kMSE, kErrExact, GRAN, OUT);                     \
   if (metric == kMAE && prec == kErrExact) return CALL(DT, k4over6, kMAE, kErrExact, GRAN, OUT); \
   if (metric == kMAE && prec == kErrFP16) return CALL(DT, k4over6, kMAE, kErrFP16, GRAN, OUT);   \
   if (metric == kMSE && prec == kErrExact) return CALL(DT, k4over6, kMSE, kErrExact, GRAN, OUT); \
   return CALL(DT, k4over6, kMSE, kErrFP16, GRAN, OUT);
 
-#define FOS_DTYPES(GRAN, OUT, CALL)                       \
-  if (dt == kBF16) { FOS_MODES(kBF16, GRAN, OUT, CALL) } \
-  if (dt == kFP16) { FOS_MODES(kFP16, GRAN, OUT, CALL) } \
-  { FOS_MODES(kFP32, GRAN, OUT, CALL) }
+#define FOS_DTYPES(MODES, GRAN, OUT, CALL)           \
+  if (dt == kBF16) { MODES(kBF16, GRAN, OUT, CALL) } \
+  if (dt == kFP16) { MODES(kFP16, GRAN, OUT, CALL) } \
+  { MODES(kFP32, GRAN, OUT, CALL) }
 
-#define CALL_Q1(DT, R, M, P, G, O) launch_1x16_t<1, DT, R, M, P, G, O>(a, s)
-#define CALL_QL(DT, R, M, P, G, O) launch_1x16_t<kMaxList, DT, R, M, P, G, O>(a, s)
-#define CALL_T(DT, R, M, P, G, O) launch_16x16_t<DT, R, M, P, G, O>(a, s)
+#define CALL_Q1(DT, R, M, P, O, G, OUT) launch_1x16_t<1, DT, R, M, P, O, G, OUT>(a, s)
+#define CALL_QL(DT, R, M, P, O, G, OUT) launch_1x16_t<kMaxList, DT, R, M, P, O, G, OUT>(a, s)
+#define CALL_F(DT, R, M, P, O, G, OUT) launch_fused_t<DT, R, M, P, O, G, OUT>(a, ws, amax_out, s)
+#define CALL_T(DT, R, M, P, G, OUT) launch_16x16_t<DT, R, M, P, G, OUT>(a, s)
 
-hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int gran, const Args1x16<1>& a,
+hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int order, int gran, const Args1x16<1>& a,
                              hipStream_t s) {
-  if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, CALL_Q1) }
-  if (gran == kGranRow) { FOS_DTYPES(kGranRow, kOutQuant, CALL_Q1) }
-  FOS_DTYPES(kGranGroup, kOutQuant, CALL_Q1)
+  if (gran == kGranTensor) { FOS_DTYPES(FOS_MODES, kGranTensor, kOutQuant, CALL_Q1) }
+  if (gran == kGranRow) { FOS_DTYPES(FOS_MODES, kGranRow, kOutQuant, CALL_Q1) }
+  FOS_DTYPES(FOS_MODES, kGranGroup, kOutQuant, CALL_Q1)
 }
 
-#define CALL_F(DT, R, M, P, G, O) launch_fused_t<DT, R, M, P, G, O>(a, ws, amax_out, s)
-
-hipError_t launch_fused(int dt, int recipe, int metric, int prec, const Args1x16<1>& a, uint32_t* ws,
+hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                         float* amax_out, hipStream_t s) {
-  FOS_DTYPES(kGranTensor, kOutQuant, CALL_F)
+  FOS_DTYPES(FOS_MODES, kGranTensor, kOutQuant, CALL_F)
 }
 
-hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, const Args1x16<kMaxList>& a, hipStream_t s) {
-  if (dt == kBF16) { FOS_MODES(kBF16, kGranTensor, kOutQdq, CALL_QL) }
-  FOS_MODES(kFP16, kGranTensor, kOutQdq, CALL_QL)
+hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, int gran,
+                           const Args1x16<kMaxList>& a, hipStream_t s) {
+  if (gran == kGranTensor) { FOS_DTYPES(FOS_MODES, kGranTensor, kOutQdq, CALL_QL) }
+  FOS_DTYPES(FOS_MODES, kGranRow, kOutQdq, CALL_QL)
 }
 
-hipError_t launch_quant_16x16(int dt, int recipe, int metric, int prec, int gran, const Args16x16& a, hipStream_t s) {
-  if (gran == kGranTensor) { FOS_DTYPES(kGranTensor, kOutQuant, CALL_T) }
-  FOS_DTYPES(kGranRow, kOutQuant, CALL_T)
+hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int out, const Args16x16& a,
+                        hipStream_t s) {
+  if (out == kOutQuant) {
+    if (gran == kGranTensor) { FOS_DTYPES(FOS_MODES_T, kGranTensor, kOutQuant, CALL_T) }
+    FOS_DTYPES(FOS_MODES_T, kGranRow, kOutQuant, CALL_T)
+  }
+  if (gran == kGranTensor) { FOS_DTYPES(FOS_MODES_T, kGranTensor, kOutQdq, CALL_T) }
+  FOS_DTYPES(FOS_MODES_T, kGranRow, kOutQdq, CALL_T)
 }
 
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,

@@ -90,8 +90,9 @@ def test_weights_16x16(orc, dtype, M, K, seed):
 
 # ------------------------------------------------------------------ fused QDQ over the expert list
 
+@pytest.mark.parametrize("order", ["tree", "seq"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_qdq_expert_list_8x2048x7168(orc, dtype):
+def test_qdq_expert_list_8x2048x7168(orc, dtype, order):
     lst = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=(dtype,))[dtype]
     bits = [raw_bits(t) for t in lst]
     xs = [t.to("cuda") for t in lst]
@@ -99,8 +100,9 @@ def test_qdq_expert_list_8x2048x7168(orc, dtype):
     ams_d = [torch.from_numpy(a).to("cuda") for a in ams]
     ys = [torch.empty_like(t) for t in xs]
     rows = [sample_rows(2048, 12, 100 + i) for i in range(8)]
-    for (recipe, metric, prec), bound in itertools.product(MODES, BOUNDS):
-        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+    modes = MODES if order == "tree" else [m for m in MODES if m[0] == "4over6"]
+    for (recipe, metric, prec), bound in itertools.product(modes, BOUNDS):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, err_order=order)
         fos.fos_qdq_list(xs, ams_d, outs=ys, **kw)
         torch.cuda.synchronize()
         for i in range(8):

@@ -24,6 +24,13 @@ def dev(t):
     return t.to("cuda")
 
 
+def u_bits(a: np.ndarray) -> np.ndarray:
+    """Integer view of raw element bits (fp32 arrays as uint32), so that
+    comparisons are bitwise: signed zeros and NaN payloads included."""
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
 def bits_of(t: torch.Tensor) -> np.ndarray:
     return raw_bits(t.cpu())
 
@@ -295,9 +302,9 @@ def test_rejects_bad_arguments():
     with pytest.raises(fos.FosError):
         fos.fos_quantize(x, a, bound=300)
     with pytest.raises(fos.FosError):
-        fos.fos_qdq(torch.zeros(16, 64, dtype=torch.float32, device="cuda"), a)  # fp32 QDQ
+        fos.fos_quantize(x, a, block="16x16", err_order="seq")  # the sequential order is 1x16 only
     with pytest.raises(fos.FosError):
-        fos.fos_qdq(x, a, block="16x16")
+        fos.fos_qdq(x, a, block="16x16", err_order="seq")
     flat = torch.zeros(16 * 64 + 8, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fos.FosError):
         fos.fos_quantize(flat[1:1 + 16 * 64].view(16, 64), a)  # misaligned
@@ -366,3 +373,64 @@ def test_fused_nan_inf_tensors(orc):
         np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
         np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
         np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+
+
+# ------------------------------------------------------------------ sequential order, wider QDQ
+
+SEQ_MODES = [("4over6", m, p) for m in ("mae", "mse") for p in ("exact", "fp16")]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_sequential_order_every_entry(orc, dtype):
+    """The sequential error order through quantize (per tensor and per row),
+    QDQ, the grouped call and the fused call, on ragged shapes."""
+    M, K = 67, 1552
+    x = _family("outlier", dtype, M, K, 71)
+    b = raw_bits(x)
+    am = {"tensor": orc.amax(b, dtype, "tensor"), "row": orc.amax(b, dtype, "row")}
+    for (recipe, metric, prec), bound in itertools.product(SEQ_MODES, (448, 256)):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, err_order="seq")
+        for gran in ("tensor", "row"):
+            assert_quant_equal(orc, x, dtype, am[gran], label="seq", scale_gran=gran, **kw)
+            y = fos.fos_qdq(dev(x), dev(torch.from_numpy(am[gran])), scale_gran=gran, **kw)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(u_bits(bits_of(y)), u_bits(orc.qdq(b, dtype, am[gran], scale_gran=gran, **kw)))
+        codes, scales, amax, _ = fos.fos_quantize_fused(dev(x), **kw)
+        torch.cuda.synchronize()
+        want = orc.quantize(b, dtype, am["tensor"], **kw)
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+    # grouped
+    offs = np.array([16, 16, 48, 64], np.int32)
+    gam = np.array([orc.amax(b[s:e], dtype, "tensor")[0] if e > s else 0.0
+                    for s, e in zip([0, 16, 16, 48], offs)], np.float32)
+    for recipe, metric, prec in SEQ_MODES:
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, err_order="seq")
+        want = orc.quantize_grouped(b, dtype, offs, gam, **kw)
+        codes, scales, _ = fos.fos_quantize_grouped(dev(x), dev(torch.from_numpy(offs)), dev(torch.from_numpy(gam)),
+                                                    **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("block,gran", [("1x16", "tensor"), ("1x16", "row"), ("16x16", "tensor"), ("16x16", "row")])
+def test_qdq_every_dtype_block_and_granularity(orc, dtype, block, gran):
+    """Fused QDQ beyond the page's bf16/fp16 1x16 per-tensor path: fp32,
+    row-scaled and 16x16, against the oracle's QDQ, as one tensor and as a
+    list of tensors of different shapes."""
+    shapes = [(48, 272), (16, 16), (96, 1040)]
+    xs = [_family(f, dtype, M, K, 80 + i) for i, ((M, K), f) in enumerate(zip(shapes, ("weight", "outlier", "special")))]
+    bs = [raw_bits(x) for x in xs]
+    mode = "tensor" if gran == "tensor" else ("band16" if block == "16x16" else "row")
+    ams = [orc.amax(b, dtype, mode) for b in bs]
+    for (recipe, metric, prec), bound in itertools.product(MODES, (448, 256)):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, block=block, scale_gran=gran)
+        ys = fos.fos_qdq_list([dev(x) for x in xs], [dev(torch.from_numpy(a)) for a in ams], **kw)
+        y0 = fos.fos_qdq(dev(xs[0]), dev(torch.from_numpy(ams[0])), **kw)
+        torch.cuda.synchronize()
+        for i in range(len(xs)):
+            np.testing.assert_array_equal(u_bits(bits_of(ys[i])), u_bits(orc.qdq(bs[i], dtype, ams[i], **kw)),
+                                          err_msg=f"{i} {kw}")
+        np.testing.assert_array_equal(u_bits(bits_of(y0)), u_bits(orc.qdq(bs[0], dtype, ams[0], **kw)))
