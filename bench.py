@@ -463,6 +463,17 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
     out["amax_then_quantize_bf16_8192x4096"] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb + 2 * n, avg)}
     log(f"[bench] fos_amax + fos_quantize (two launches): {avg * 1e3:.1f} us")
 
+    # nvfp4_dequantize of the step's outputs back to bf16 (the dequantized-
+    # backward recompute): reads 0.5625 B/elem, writes 2 B/elem
+    ys = [torch.empty_like(x) for x in xs]
+    _, ms = time_loop(lambda i: fos.nvfp4_dequantize(codes[i], scales[i], sdec[i], "tensor", torch.bfloat16,
+                                                     out=ys[i]), len(xs), 200, 10)
+    avg = float(np.median(ms))
+    out["dequantize_bf16_8192x4096"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
+                                        "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
+    log(f"[bench] dequantize bf16 8192x4096: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
+    del ys
+
     # 16x16 weights, bf16 4096x14336 and fp32 4096x4096, per-tensor, MSE exact, 448
     for dtype, (M, K) in (("bf16", (4096, 14336)), ("fp32", (4096, 4096))):
         w = synthdata.weight(M, K, 31, dtype).to("cuda")

@@ -282,10 +282,8 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t M, int
   if (!aligned(codes, 8) || !aligned(y, 16) || !aligned(sdec, 4)) return fail(FOS_ERR_ALIGN, "misaligned pointer");
   if ((rc = check_device())) return rc;
   if (M * K == 0) return FOS_OK;
-  const int64_t nblk = M * (K / 16);
   return launch_status(fos::launch_dequant(out_dtype, scale_gran == FOS_PER_ROW ? fos::kGranRow : fos::kGranTensor,
-                                           codes, scales, sdec, M, K, y, grid_for((nblk + 63) / 64),
-                                           static_cast<hipStream_t>(stream)));
+                                           codes, scales, sdec, M, K, y, static_cast<hipStream_t>(stream)));
 }
 
 int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,

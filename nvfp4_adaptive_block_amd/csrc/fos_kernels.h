@@ -88,7 +88,7 @@ hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, 
 hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int out, const Args16x16& a,
                         hipStream_t s);
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,
-                          int64_t M, int64_t K, void* y, int grid, hipStream_t s);
+                          int64_t M, int64_t K, void* y, hipStream_t s);
 hipError_t launch_amax(int dt, int gran, const void* x, int64_t M, int64_t K, float* out, int grid, hipStream_t s);
 hipError_t launch_zero_u32(void* p, int64_t n, hipStream_t s);
 

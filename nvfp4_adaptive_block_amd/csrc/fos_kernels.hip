@@ -126,6 +126,27 @@ template <> __device__ __forceinline__ void store16<kFP32>(Rsrc r, uint32_t off,
   }
 }
 
+// Store 8 decoded values as the output type.
+template <int DT> __device__ __forceinline__ void store8(Rsrc r, uint32_t off, const float* y);
+template <> __device__ __forceinline__ void store8<kBF16>(Rsrc r, uint32_t off, const float* y) {
+  const v4i a = {(int)pack_bf16(y[0], y[1]), (int)pack_bf16(y[2], y[3]), (int)pack_bf16(y[4], y[5]),
+                 (int)pack_bf16(y[6], y[7])};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+}
+template <> __device__ __forceinline__ void store8<kFP16>(Rsrc r, uint32_t off, const float* y) {
+  const v4i a = {(int)pack_f16(y[0], y[1]), (int)pack_f16(y[2], y[3]), (int)pack_f16(y[4], y[5]),
+                 (int)pack_f16(y[6], y[7])};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+}
+template <> __device__ __forceinline__ void store8<kFP32>(Rsrc r, uint32_t off, const float* y) {
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const v4i a = {__float_as_int(y[4 * i]), __float_as_int(y[4 * i + 1]), __float_as_int(y[4 * i + 2]),
+                   __float_as_int(y[4 * i + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * i, 0, 0);
+  }
+}
+
 __device__ __forceinline__ void store_codes(Rsrc r, uint32_t off, uint32_t c0, uint32_t c1) {
   const v2i v = {(int)c0, (int)c1};
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
@@ -804,20 +825,72 @@ template <> __device__ __forceinline__ void put16<kFP32>(void* base, int64_t idx
 }
 
 
+// Decode: one lane per half block (8 elements), so that a wave's output
+// store is 1 KiB contiguous (16-bit types) and its code load 256 B. A unit
+// is 32 blocks of the flattened tensor, or of one row for per-row S_dec;
+// waves take units grid-stride, kDqU units per step with all their loads
+// issued first. Loads and stores are raw buffer operations (past the end:
+// zeros read, stores dropped).
+constexpr int kDqU = 4;
+
 template <int DT, int GRAN>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                                 const float* __restrict__ sdec, int64_t M, int64_t K, void* y) {
-  const int64_t nbk = K >> 4;
-  const int64_t nblk = M * nbk;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-    const int64_t row = b / nbk;
-    const float S_dec = (GRAN == kGranTensor) ? sdec[0] : sdec[row];
-    const uint2 c = *reinterpret_cast<const uint2*>(codes + b * 8);
-    const float D = e4m3_value(scales[b]) * S_dec;
-    float xh[16];
-    decode16(c.x, c.y, D, xh);
-    put16<DT>(y, b * 16, xh);
+                                                 const float* __restrict__ sdec, int64_t M, int64_t K, void* y,
+                                                 int64_t total_units) {
+  constexpr int kOH = Raw<DT>::kBytes / 2;  // output bytes per half block
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t nbk = K >> 4, nblk = M * nbk;
+  const int64_t spr = (nbk + 31) / 32;  // units per row (per-row S_dec)
+  const uint32_t off_c = lane * 4, off_s = lane >> 1, off_y = lane * kOH;
+  // per-row units: (row, segment) of the first unit, advanced by whole steps
+  // of nwaves units without dividing per unit
+  const int64_t q1 = nwaves / spr, r1 = nwaves - q1 * spr;
+  const int64_t first = (int64_t)blockIdx.x * 4 + wv;
+  int64_t row0 = (GRAN == kGranTensor) ? 0 : first / spr;
+  int64_t seg0 = (GRAN == kGranTensor) ? 0 : first - row0 * spr;
+  for (int64_t u0 = first; u0 < total_units; u0 += nwaves * kDqU) {
+    Rsrc rc[kDqU], ry[kDqU];
+    uint32_t c[kDqU], sc[kDqU];
+    float S_dec[kDqU];
+    int64_t row = row0, seg = seg0;
+#pragma unroll
+    for (int j = 0; j < kDqU; j++) {
+      const int64_t u = u0 + j * nwaves;
+      const bool valid = u < total_units;
+      int64_t b0, nvalid;
+      if (GRAN == kGranTensor) {
+        b0 = u * 32;
+        nvalid = min((int64_t)32, nblk - b0);
+      } else {
+        b0 = row * nbk + seg * 32;
+        nvalid = min((int64_t)32, nbk - seg * 32);
+      }
+      if (!valid) nvalid = 0;
+      rc[j] = make_rsrc(codes + b0 * 8, nvalid * 8);
+      const Rsrc rs = make_rsrc(scales + b0, nvalid);
+      ry[j] = make_rsrc(static_cast<char*>(y) + b0 * 2 * kOH, nvalid * 2 * kOH);
+      c[j] = __builtin_amdgcn_raw_buffer_load_b32(rc[j], off_c, 0, 0);
+      sc[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, off_s, 0, 0);
+      S_dec[j] = (GRAN == kGranTensor) ? ld_const(sdec, 0) : (valid ? ld_const(sdec, row) : 1.0f);
+      if (GRAN != kGranTensor) {  // to the unit nwaves further on
+        row += q1;
+        seg += r1;
+        if (seg >= spr) { seg -= spr; ++row; }
+      }
+    }
+    row0 = row;
+    seg0 = seg;
+#pragma unroll
+    for (int j = 0; j < kDqU; j++) {
+      float q[8];
+      e2m1_unpack8(c[j], q);
+      const float D = e4m3_value(sc[j]) * S_dec[j];
+#pragma unroll
+      for (int i = 0; i < 8; i++) q[i] = q[i] * D;
+      store8<DT>(ry[j], off_y, q);
+    }
   }
 }
 
@@ -1222,9 +1295,21 @@ hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int 
   FOS_DTYPES(FOS_MODES_T, kGranRow, kOutQdq, CALL_T)
 }
 
+template <int DT, int GRAN>
+static hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* scales, const float* sdec, int64_t M,
+                                   int64_t K, void* y, hipStream_t s) {
+  const int64_t nbk = K / 16;
+  const int64_t units = (GRAN == kGranTensor) ? (M * nbk + 31) / 32 : M * ((nbk + 31) / 32);
+  // many workgroups: a write-heavy stream keeps more stores in flight that way
+  const int64_t grid = max((int64_t)1, min((int64_t)8192, (units + 4 * kDqU - 1) / (4 * kDqU)));
+  hipLaunchKernelGGL((k_dequant<DT, GRAN>), dim3((unsigned)grid), dim3(256), 0, s, codes, scales, sdec, M, K, y,
+                     units);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,
-                          int64_t M, int64_t K, void* y, int grid, hipStream_t s) {
-#define FOS_DQ(DT, G) hipLaunchKernelGGL((k_dequant<DT, G>), dim3(grid), dim3(256), 0, s, codes, scales, sdec, M, K, y)
+                          int64_t M, int64_t K, void* y, hipStream_t s) {
+#define FOS_DQ(DT, G) return launch_dequant_t<DT, G>(codes, scales, sdec, M, K, y, s)
   if (dt == kBF16) { if (gran == kGranTensor) FOS_DQ(kBF16, kGranTensor); else FOS_DQ(kBF16, kGranRow); }
   else if (dt == kFP16) { if (gran == kGranTensor) FOS_DQ(kFP16, kGranTensor); else FOS_DQ(kFP16, kGranRow); }
   else { if (gran == kGranTensor) FOS_DQ(kFP32, kGranTensor); else FOS_DQ(kFP32, kGranRow); }

@@ -152,6 +152,16 @@ def grouped_tokens(M: int, pad: int, K: int, G: int, seeds=(51, 52, 53, 54), dty
     return x.to(TORCH_DTYPES[dtype]), offs, fac
 
 
+def random_packed_codes(M: int, K: int, seed: int) -> np.ndarray:
+    """uint8 [M, K/2] of uniformly random bytes (two random 4-bit codes each)."""
+    return np.random.default_rng(seed).integers(0, 256, (M, K // 2), dtype=np.uint8)
+
+
+def random_block_scales(M: int, K: int, seed: int) -> np.ndarray:
+    """uint8 [M, K/16] of uniformly random finite non-negative E4M3 codes (0x00..0x7E)."""
+    return np.random.default_rng(seed).integers(0, 0x7F, (M, K // 16), dtype=np.uint8)
+
+
 def raw_bits(t: torch.Tensor) -> np.ndarray:
     """Host numpy view of a tensor's raw element bits: uint16 for bfloat16
     and float16, float32 for float32."""

@@ -170,3 +170,27 @@ def test_fused_dense_activation_8192x4096(orc):
         np.testing.assert_array_equal(c2.cpu().numpy(), w2["codes"])
         np.testing.assert_array_equal(s2.cpu().numpy(), w2["scales"])
     assert not ws[256:].any()
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("gran", ["tensor", "row"])
+def test_dequantize_8192x4096(orc, out_dtype, gran):
+    """nvfp4_dequantize of the dense-activation shape from random codes (every
+    nibble value) and random finite E4M3 scales, in the launch configuration
+    the benchmark times; sampled rows against the oracle's decode."""
+    M, K = 8192, 4096
+    codes = synthdata.random_packed_codes(M, K, 91)
+    scales = synthdata.random_block_scales(M, K, 92)
+    rng = np.random.default_rng(93)
+    if gran == "tensor":
+        sdec = np.array([0.37], np.float32)
+    else:
+        sdec = (10.0 ** rng.uniform(-3, 3, M)).astype(np.float32)
+    y = fos.nvfp4_dequantize(torch.from_numpy(codes).to("cuda"), torch.from_numpy(scales).to("cuda"),
+                             torch.from_numpy(sdec).to("cuda"), gran, synthdata.TORCH_DTYPES[out_dtype])
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 64, 94)
+    want = orc.dequantize(codes[rows], scales[rows], sdec if gran == "tensor" else sdec[rows], gran, out_dtype)
+    got = raw_bits(y.cpu())[rows]
+    view = np.uint32 if out_dtype == "fp32" else np.uint16
+    np.testing.assert_array_equal(np.ascontiguousarray(got).view(view), np.ascontiguousarray(want).view(view))
