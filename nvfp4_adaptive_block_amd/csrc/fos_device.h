@@ -152,15 +152,15 @@ __device__ __forceinline__ float tree16(float* u) {
   return u[0];
 }
 
-// Cross-lane moves within a DPP row of 16 lanes (register-to-register, no
-// LDS): row_shl:n (lane i reads lane i + n of its row; lanes past the row's
-// end read 0), row_ror:n (rotate within the row) and row_newbcast:n (every
-// lane reads lane n of its row).
+// Cross-lane moves (register-to-register, no LDS): CTRL is a DPP control,
+// e.g. quad_perm [a,b,c,d] = a | b << 2 | c << 4 | d << 6 (each lane of a
+// group of four reads the lane the pattern names) or row_shl:n = 0x100 + n
+// (lane i reads lane i + n of its 16-lane row; past the row's end: 0).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-constexpr int kDppRowShl = 0x100, kDppRowRor = 0x120, kDppRowBcast = 0x150;
+constexpr int kDppRowShl = 0x100;
 
 // The sequential order: the sixteen terms added left to right in element
 // order (Transformer Engine's order, kept by the Megatron-LM page).
@@ -169,28 +169,6 @@ __device__ __forceinline__ float seq16(const float* u) {
 #pragma unroll
   for (int i = 1; i < 16; i++) s = s + u[i];
   return s;
-}
-
-// The same tree across the 16 lanes of a DPP row (lanes 16k .. 16k+15 hold
-// terms 0..15): at each stride s (8, 4, 2, 1) lane i adds lane i + s, so
-// lane 16k ends with the pinned sum; the result is then broadcast to all 16
-// lanes of the row. (Lanes other than 16k add values that never reach it.)
-__device__ __forceinline__ float tree16_lanes(float v) {
-  v = v + dpp<kDppRowShl + 8>(v);
-  v = v + dpp<kDppRowShl + 4>(v);
-  v = v + dpp<kDppRowShl + 2>(v);
-  v = v + dpp<kDppRowShl + 1>(v);
-  return dpp<kDppRowBcast + 0>(v);
-}
-
-// Max over the 16 lanes of a DPP row, on every lane (max is exact and
-// order-free, so rotations serve).
-__device__ __forceinline__ float max16_lanes(float v) {
-  v = __builtin_fmaxf(v, dpp<kDppRowRor + 8>(v));
-  v = __builtin_fmaxf(v, dpp<kDppRowRor + 4>(v));
-  v = __builtin_fmaxf(v, dpp<kDppRowRor + 2>(v));
-  v = __builtin_fmaxf(v, dpp<kDppRowRor + 1>(v));
-  return v;
 }
 
 }  // namespace fos

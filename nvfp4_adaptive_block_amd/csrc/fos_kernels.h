@@ -34,14 +34,6 @@ __host__ __device__ constexpr int unit_blocks(int out, int dt) {
   return 64 * ((out == kOutQuant && dt != kFP32) ? 2 : 1);
 }
 
-// Row segments per lane in one unit of the 16x16 kernel: a unit is one
-// 16-row band times 4 * NB consecutive tiles (lane = 16 * tile + row, the
-// lane's j-th segment in tile 4j + lane / 16). 16-bit inputs keep two
-// segments per lane in flight, fp32 inputs and the fused QDQ one.
-__host__ __device__ constexpr int tile_segs(int out, int dt) {
-  return (out == kOutQuant && dt != kFP32) ? 2 : 1;
-}
-
 // One tensor of a 1x16 launch. unit_begin: index of its first 64-block unit
 // in the launch's unit space.
 struct TensorRef {

@@ -346,64 +346,6 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
   }
 }
 
-// Quantize one 16x16 tile: this lane holds one 16-element row segment, the
-// 16 lanes of its DPP row hold the tile's rows 0..15 in lane order. The tile
-// amax is the max over the lanes; each lane sums its row's error terms with
-// the pinned tree, and the lane sums are combined with the same tree in row
-// order. The result (kept candidate) is the same on all 16 lanes.
-template <int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, bool TAB, bool SEQ>
-__device__ __forceinline__ bool tile_16x16(const float* x, float S_enc, float S_dec, const Table& tab, BlockOut& o,
-                                           float* xh) {
-  const float a = max16_lanes(amax16<CAREFUL>(x));
-  const Cand k6 = make_cand<TAB>(div6(a), S_enc, S_dec, tab);
-  uint32_t c60, c61;
-  encode16<CAREFUL>(x, k6.E, c60, c61);
-  if (RECIPE == kNVFP4) {
-    o.c0 = c60; o.c1 = c61; o.scale = k6.scale;
-    if (NEED_XHAT) decode16(c60, c61, k6.D, xh);
-    if (CAREFUL) return true;
-    const float n = any_nan16(x) ? 1.0f : 0.0f;
-    return max16_lanes(n) == 0.0f;
-  } else {
-    float e6, e4;
-    uint32_t c40, c41;
-    Cand k4;
-    if (SEQ) {
-      // one candidate after the other (fewer live registers)
-      {
-        float t[16];
-        decode16(c60, c61, k6.D, t);
-        e6 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, t));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
-      encode16<CAREFUL>(x, k4.E, c40, c41);
-      {
-        float t[16];
-        decode16(c40, c41, k4.D, t);
-        e4 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, t));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      // both at once: the two cross-lane trees interleave, which hides the
-      // DPP read-after-write stalls of each
-      k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
-      encode16<CAREFUL>(x, k4.E, c40, c41);
-      float xh6[16], xh4[16];
-      decode16(c60, c61, k6.D, xh6);
-      decode16(c40, c41, k4.D, xh4);
-      e6 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, xh6));
-      e4 = tree16_lanes(err16<METRIC, PREC, kOrderTree>(x, xh4));
-    }
-    const bool four = e4 < e6;
-    o.c0 = four ? c40 : c60;
-    o.c1 = four ? c41 : c61;
-    o.scale = four ? k4.scale : k6.scale;
-    if (NEED_XHAT) decode16(o.c0, o.c1, four ? k4.D : k6.D, xh);
-    return CAREFUL || (e6 == e6 && e4 == e4);
-  }
-}
-
 // Quantize a 1x16 block with the fast form, falling back to the careful form
 // when the block holds a NaN.
 template <int RECIPE, int METRIC, int PREC, int ORDER, bool NEED_XHAT, bool TAB>
@@ -649,27 +591,167 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
   walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, 0.0f);
 }
 
+// NaN-dropping magnitude max over packed 16-bit pairs: with m = |h| bits,
+// adding `bias` (0x7F for bf16, 0x3FF for f16) sends exactly the NaN patterns
+// past 0x7FFF, where a signed 16-bit max ignores them.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ s16x2 pair_key(uint32_t w) {
+  const uint32_t bias = (DT == kBF16) ? 0x007F007Fu : 0x03FF03FFu;
+  return __builtin_bit_cast(s16x2, w & 0x7FFF7FFFu) + __builtin_bit_cast(s16x2, bias);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pair_key_to_f32_bits(s16x2 k) {
+  const int bias = (DT == kBF16) ? 0x7F : 0x3FF;
+  const int m = max((int)k.x, (int)k.y) - bias;  // magnitude bits of the max
+  if (DT == kBF16) return (uint32_t)m << 16;
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)m);
+  return __float_as_uint((float)h);
+}
+
 // ------------------------------------------------------------ 16x16 kernel
 
-// A unit is one 16-row band times 4 * kS consecutive tiles: lane = 16 * tile +
-// row in tile for each of the lane's kS segments, so a wave reads 16 rows x
-// 64 * kS columns. Lanes of a ragged last group of tiles idle with
-// out-of-range offsets.
+// A 16x16 tile belongs to LPT = 4 consecutive lanes: lane j of the group
+// holds the tile's rows j, j + 4, j + 8, j + 12 (RPL = 4 rows of 16
+// elements each). A wave's unit is one 16-row band times 16 consecutive
+// tiles, so each load instruction covers 4 rows, each over 512 (bf16) or
+// 1024 (fp32) contiguous bytes, instead of 16 rows.
+//
+// The pinned error order over a tile is the width-16 tree applied to the
+// sixteen row sums in row order. Its levels of stride 8, 4 (and 2 when
+// LPT = 2) pair rows of the same residue mod LPT, so they run inside a lane
+// over the lane's own row sums (local strides 8 / LPT, ...); the remaining
+// levels (stride LPT / 2, ..., 1) pair lanes of the group and run as DPP row
+// shifts; the group's first lane then holds the pinned sum and a quad
+// permute broadcasts it. The tile amax is the lane's max over its rows, then
+// over the group.
+template <int DT> struct Tile16 {
+  // lanes per tile: 4 (2 for 16-bit inputs halves the rows per load
+  // instruction but needs twice the registers for a tile's raw rows, which
+  // costs more occupancy than the access pattern gains)
+  static constexpr int kLPT = 4;
+  static constexpr int kRPL = 16 / kLPT;              // rows per lane
+  static constexpr int kTiles = 64 / kLPT;            // tiles per unit
+};
+
+// max over the lanes of a tile group
+template <int LPT>
+__device__ __forceinline__ float group_max(float v) {
+  v = __builtin_fmaxf(v, dpp<0xB1>(v));                      // quad_perm [1,0,3,2]
+  if (LPT == 4) v = __builtin_fmaxf(v, dpp<0x4E>(v));        // quad_perm [2,3,0,1]
+  return v;
+}
+
+// The pinned tree's remaining levels across the group, then the group's
+// first lane broadcast to the group.
+template <int LPT>
+__device__ __forceinline__ float group_tree(float v) {
+  if (LPT == 4) v = v + dpp<kDppRowShl + 2>(v);
+  v = v + dpp<kDppRowShl + 1>(v);
+  return LPT == 4 ? dpp<0x00>(v) : dpp<0xA0>(v);             // quad_perm [0,0,0,0] / [0,0,2,2]
+}
+
+// The in-lane levels of the pinned tree over N local row sums (strides N/2,
+// ..., 1: position i adds position i + stride). Overwrites w.
+template <int N>
+__device__ __forceinline__ float lane_tree(float* w) {
+#pragma unroll
+  for (int s = N / 2; s >= 1; s >>= 1)
+#pragma unroll
+    for (int i = 0; i < s; i++) w[i] = w[i] + w[i + s];
+  return w[0];
+}
+
+// Quantize the lane's rows of one tile. raw[i] holds row j + LPT i.
+// Returns false when the fast form cannot be trusted (a NaN in the tile);
+// the caller then reruns with CAREFUL. The kept candidate is the same on all
+// lanes of the group.
+template <int DT, int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT>
+__device__ __forceinline__ bool tile_rows(const Raw<DT>* raw, float S_enc, float S_dec, const Table& tab,
+                                          uint32_t (*codes)[2], uint32_t& scale, float (*xh)[16]) {
+  constexpr int kLPT = Tile16<DT>::kLPT, kRPL = Tile16<DT>::kRPL;
+  // NaN-dropping tile amax; 16-bit inputs straight from their bits (no
+  // unpacked row stays live for the encode loop)
+  float a = 0.0f;
+  if constexpr (DT == kFP32) {
+#pragma unroll
+    for (int i = 0; i < kRPL; i++) {
+      float x[16];
+      raw[i].unpack(x);
+      a = __builtin_fmaxf(a, amax16<true>(x));
+    }
+  } else {
+    s16x2 k = pair_key<DT>(0u);
+#pragma unroll
+    for (int i = 0; i < kRPL; i++) {
+      const uint32_t w[8] = {(uint32_t)raw[i].a.x, (uint32_t)raw[i].a.y, (uint32_t)raw[i].a.z, (uint32_t)raw[i].a.w,
+                             (uint32_t)raw[i].b.x, (uint32_t)raw[i].b.y, (uint32_t)raw[i].b.z, (uint32_t)raw[i].b.w};
+#pragma unroll
+      for (int t = 0; t < 8; t++) k = __builtin_elementwise_max(k, pair_key<DT>(w[t]));
+    }
+    a = __uint_as_float(pair_key_to_f32_bits<DT>(k));
+  }
+  a = group_max<kLPT>(a);
+  const Cand k6 = make_cand<true>(div6(a), S_enc, S_dec, tab);
+  if (RECIPE == kNVFP4) {
+    float nan = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRPL; i++) {
+      float x[16];
+      raw[i].unpack(x);
+      encode16<CAREFUL>(x, k6.E, codes[i][0], codes[i][1]);
+      if (NEED_XHAT) decode16(codes[i][0], codes[i][1], k6.D, xh[i]);
+      if (!CAREFUL && any_nan16(x)) nan = 1.0f;
+    }
+    scale = k6.scale;
+    return CAREFUL || group_max<kLPT>(nan) == 0.0f;
+  } else {
+    const Cand k4 = make_cand<true>(a * 0.25f, S_enc, S_dec, tab);
+    float r6[kRPL], r4[kRPL];
+    uint32_t c4[kRPL][2];
+#pragma unroll
+    for (int i = 0; i < kRPL; i++) {
+      float x[16], t[16];
+      raw[i].unpack(x);
+      encode16<CAREFUL>(x, k6.E, codes[i][0], codes[i][1]);
+      decode16(codes[i][0], codes[i][1], k6.D, t);
+      r6[i] = err16<METRIC, PREC, kOrderTree>(x, t);
+      encode16<CAREFUL>(x, k4.E, c4[i][0], c4[i][1]);
+      decode16(c4[i][0], c4[i][1], k4.D, t);
+      r4[i] = err16<METRIC, PREC, kOrderTree>(x, t);
+      __builtin_amdgcn_sched_barrier(0);  // one row at a time (register pressure)
+    }
+    const float e6 = group_tree<kLPT>(lane_tree<kRPL>(r6));
+    const float e4 = group_tree<kLPT>(lane_tree<kRPL>(r4));
+    const bool four = e4 < e6;
+#pragma unroll
+    for (int i = 0; i < kRPL; i++) {
+      codes[i][0] = four ? c4[i][0] : codes[i][0];
+      codes[i][1] = four ? c4[i][1] : codes[i][1];
+      if (NEED_XHAT) decode16(codes[i][0], codes[i][1], four ? k4.D : k6.D, xh[i]);
+    }
+    scale = four ? k4.scale : k6.scale;
+    return CAREFUL || (e6 == e6 && e4 == e4);
+  }
+}
+
 template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   __shared__ float lds[4][256];
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kEB = kB / 16;  // bytes per element
   constexpr bool kXhat = OUT == kOutQdq;
-  constexpr int kS = tile_segs(OUT, DT);
+  constexpr int kLPT = Tile16<DT>::kLPT, kRPL = Tile16<DT>::kRPL, kT = Tile16<DT>::kTiles;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const Table tab{lds[wv], lds[wv] + 128};
-  const int r16 = lane & 15, tq = lane >> 4;
+  const int jr = lane % kLPT, tl = lane / kLPT;  // first row in the tile, tile in the unit
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t K = args.K, nbk = K >> 4;
-  const int64_t gpb = (nbk + 4 * kS - 1) / (4 * kS);  // units per band
+  const int64_t gpb = (nbk + kT - 1) / kT;  // units per band
   const int64_t total = (args.M >> 4) * gpb;
   const int64_t per = (total + nwaves - 1) / nwaves;
   int64_t u = wave * per;
@@ -698,34 +780,29 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   const int64_t x_bytes = args.M * K * kEB;
   const int64_t c_bytes = args.M * K / 2;
   const int64_t s_bytes = args.M * nbk;
+  // the lane's offsets within a unit: row jr + LPT i of tile tl
+  const uint32_t ox0 = ((uint32_t)jr * (uint32_t)K + (uint32_t)tl * 16) * kEB;
+  const uint32_t ox_step = (uint32_t)(kLPT * K * kEB);
+  const uint32_t oc0 = (uint32_t)jr * (uint32_t)(K / 2) + (uint32_t)tl * 8, oc_step = (uint32_t)(kLPT * K / 2);
+  const uint32_t os0 = (uint32_t)jr * (uint32_t)nbk + (uint32_t)tl, os_step = (uint32_t)(kLPT * nbk);
 
   struct U16 {
     Rsrc x, out, scl;
-    uint32_t ox[kS], oo[kS], os[kS];  // lane offsets of the lane's segments
+    bool active;
   };
-  // Position of a unit: its band and index within the band, advanced
-  // incrementally (no 64-bit division per unit).
   struct P16 {
     int64_t band, tg;
   };
-  // the lane's offsets within a unit (the same for every unit)
-  uint32_t lane_ox[kS], lane_oo[kS], lane_os[kS];
-#pragma unroll
-  for (int j = 0; j < kS; j++) {
-    const uint32_t tl = tq + 4 * j;  // tile within the unit
-    lane_ox[j] = ((uint32_t)r16 * (uint32_t)K + tl * 16) * kEB;
-    lane_oo[j] = (uint32_t)r16 * (uint32_t)(K / 2) + tl * 8;
-    lane_os[j] = (uint32_t)r16 * (uint32_t)nbk + tl;
-  }
   auto advance = [&](P16 p) {
     if (++p.tg == gpb) { p.tg = 0; ++p.band; }
     return p;
   };
   auto unit = [&](const P16& p, bool valid) {
-    const int64_t t0 = p.tg * 4 * kS;                 // first tile of the unit
-    const int64_t ex = p.band * 16 * K + t0 * 16;     // its first element
-    const int64_t es = p.band * 16 * nbk + t0;        // its first scale
+    const int64_t t0 = p.tg * kT;                      // first tile of the unit
+    const int64_t ex = p.band * 16 * K + t0 * 16;      // its first element
+    const int64_t es = p.band * 16 * nbk + t0;         // its first scale
     U16 r;
+    r.active = valid && (t0 + tl < nbk);
     r.x = make_rsrc(static_cast<const char*>(args.x) + ex * kEB, valid ? x_bytes - ex * kEB : 0);
     if (OUT == kOutQuant) {
       r.out = make_rsrc(args.codes + ex / 2, valid ? c_bytes - ex / 2 : 0);
@@ -734,18 +811,21 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
       r.out = make_rsrc(static_cast<char*>(args.y) + ex * kEB, valid ? x_bytes - ex * kEB : 0);
       r.scl = r.out;
     }
-#pragma unroll
-    for (int j = 0; j < kS; j++) {
-      const bool active = valid && (t0 + tq + 4 * j < nbk);
-      r.ox[j] = active ? lane_ox[j] : kOOB;
-      r.oo[j] = OUT == kOutQuant ? (active ? lane_oo[j] : kOOB) : r.ox[j];
-      r.os[j] = (OUT == kOutQuant && active) ? lane_os[j] : kOOB;
-    }
     return r;
   };
+  auto load = [&](Raw<DT>* raw, const U16& U) {
+#pragma unroll
+    for (int i = 0; i < kRPL; i++) raw[i].load(U.x, U.active ? ox0 + i * ox_step : kOOB);
+  };
 
-  auto process = [&](const Raw<DT>* raw, const P16& p, bool valid, const U16& U) {
-    if (GRAN == kGranRow && valid && p.band != cur_band) {
+  // one unit at a time: prefetching the next unit's rows costs more
+  // occupancy than the overlap gains (measured)
+  P16 p{u / gpb, u % gpb};
+  for (; u < u_end; u++) {
+    const U16 U = unit(p, true);
+    Raw<DT> raw[kRPL];
+    load(raw, U);
+    if (GRAN == kGranRow && p.band != cur_band) {
       // tile-uniform contract: the band uses its first row's amax, and a band
       // whose rows differ is flagged
       const float A = ld_const(args.amax, p.band * 16);
@@ -761,46 +841,20 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
       }
       cur_band = p.band;
     }
+    uint32_t codes[kRPL][2], scale;
+    float xh[kXhat ? kRPL : 1][16];
+    if (!tile_rows<DT, RECIPE, METRIC, PREC, false, kXhat>(raw, S_enc, S_dec, tab, codes, scale, xh))
+      tile_rows<DT, RECIPE, METRIC, PREC, true, kXhat>(raw, S_enc, S_dec, tab, codes, scale, xh);
 #pragma unroll
-    for (int j = 0; j < kS; j++) {
-      float x[16], xh[16];
-      raw[j].unpack(x);
-      BlockOut o;
-      if (!tile_16x16<RECIPE, METRIC, PREC, false, kXhat, true, (kS > 1)>(x, S_enc, S_dec, tab, o, xh))
-        tile_16x16<RECIPE, METRIC, PREC, true, kXhat, true, (kS > 1)>(x, S_enc, S_dec, tab, o, xh);
+    for (int i = 0; i < kRPL; i++) {
       if (OUT == kOutQuant) {
-        store_codes(U.out, U.oo[j], o.c0, o.c1);
-        store_scale(U.scl, U.os[j], o.scale);
+        store_codes(U.out, U.active ? oc0 + i * oc_step : kOOB, codes[i][0], codes[i][1]);
+        store_scale(U.scl, U.active ? os0 + i * os_step : kOOB, scale);
       } else {
-        store16<DT>(U.out, U.oo[j], xh);
+        store16<DT>(U.out, U.active ? ox0 + i * ox_step : kOOB, xh[i]);
       }
     }
-  };
-
-  auto load_unit = [&](Raw<DT>* r, const U16& U) {
-#pragma unroll
-    for (int j = 0; j < kS; j++) r[j].load(U.x, U.ox[j]);
-  };
-
-  // two units in flight, as in the 1x16 kernel
-  const int64_t band0 = u / gpb;
-  P16 pa{band0, u - band0 * gpb};
-  P16 pb = advance(pa);
-  U16 UA = unit(pa, true), UB = unit(pb, u + 1 < u_end);
-  Raw<DT> A[kS], B[kS];
-  load_unit(A, UA);
-  dummy_stores<kS>();
-  load_unit(B, UB);
-  for (; u < u_end; u += 2) {
-    const bool hasB = u + 1 < u_end;
-    process(A, pa, true, UA);
-    pa = advance(pb);
-    UA = unit(pa, u + 2 < u_end);
-    load_unit(A, UA);
-    process(B, pb, hasB, UB);
-    pb = advance(pa);
-    UB = unit(pb, u + 3 < u_end);
-    load_unit(B, UB);
+    p = advance(p);
   }
 }
 
@@ -895,26 +949,6 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
 }
 
 // ------------------------------------------------------------ amax
-
-// NaN-dropping magnitude max over packed 16-bit pairs: with m = |h| bits,
-// adding `bias` (0x7F for bf16, 0x3FF for f16) sends exactly the NaN patterns
-// past 0x7FFF, where a signed 16-bit max ignores them.
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-
-template <int DT>
-__device__ __forceinline__ s16x2 pair_key(uint32_t w) {
-  const uint32_t bias = (DT == kBF16) ? 0x007F007Fu : 0x03FF03FFu;
-  return __builtin_bit_cast(s16x2, w & 0x7FFF7FFFu) + __builtin_bit_cast(s16x2, bias);
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t pair_key_to_f32_bits(s16x2 k) {
-  const int bias = (DT == kBF16) ? 0x7F : 0x3FF;
-  const int m = max((int)k.x, (int)k.y) - bias;  // magnitude bits of the max
-  if (DT == kBF16) return (uint32_t)m << 16;
-  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)m);
-  return __float_as_uint((float)h);
-}
 
 // NaN-dropping |x| max as unsigned bits (NaN patterns count as +0); the
 // order of non-negative binary32 values equals the order of their bits.
@@ -1226,7 +1260,7 @@ template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 static hipError_t launch_16x16_t(const Args16x16& a, hipStream_t s) {
   auto* fn = &k_16x16<DT, RECIPE, METRIC, PREC, GRAN, OUT>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
-  constexpr int kT = 4 * tile_segs(OUT, DT);
+  constexpr int kT = Tile16<DT>::kTiles;
   const int64_t units = (a.M / 16) * ((a.K / 16 + kT - 1) / kT);
   const int64_t grid = max((int64_t)1, min(resident, (units + 3) / 4));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
