@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 << 20
 FOOTPRINT = 1 << 30            # rotate buffers up to >= 1 GiB
 METRIC = "4over6 quantize/QDQ achieved HBM GB/s and % of MI355X peak (bit-exact)"
-FUSED_KERNEL = "void fos::k_fused<0, 1, 1, 0>(fos::Args1x16<1>, unsigned int*, float*)"
-QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0>(fos::Args1x16<1>)"
+FUSED_KERNEL = "void fos::k_fused<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)"
+QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0, 0>(fos::Args1x16<1>)"
 COPY_BYTES = 256 << 20         # the profile pass's calibration copy
 # counter summaries per kernel: (file, readable workload, algorithmic bytes per launch)
 _N = 8192 * 4096
@@ -308,27 +308,34 @@ _GR = {"0": "tensor", "1": "row", "2": "grouped"}
 _OUT = {"0": "quantize", "1": "qdq"}
 
 
+_ORD = {"0": "", "1": " seq"}
+
+
 def describe_kernel(name: str) -> str:
     """Readable mode of one of this library's kernel template instances."""
     import re
-    m = re.match(r"void fos::k_1x16<(\d+), (\d), (\d), (\d), (\d), (\d), (\d)>", name)
+    m = re.match(r"void fos::k_1x16<(\d+), (\d), (\d), (\d), (\d), (\d), (\d), (\d)>", name)
     if m:
-        nt, dt, rc, mt, pr, gr, out = m.groups()
+        nt, dt, rc, mt, pr, od, gr, out = m.groups()
         lst = f" list<{nt}>" if nt != "1" else ""
-        err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
+        err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
         return f"1x16 {_OUT[out]}{lst} {_DT[dt]} {_RC[rc]}{err} {_GR[gr]}"
     m = re.match(r"void fos::k_16x16<(\d), (\d), (\d), (\d), (\d), (\d)>", name)
     if m:
         dt, rc, mt, pr, gr, out = m.groups()
         err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
         return f"16x16 {_OUT[out]} {_DT[dt]} {_RC[rc]}{err} {_GR[gr]}"
-    if "k_amax_tensor" in name:
-        return "amax per tensor (" + {"0": "bf16", "1": "fp16", "2": "fp32"}.get(name.split("<")[1][0], "?") + ")"
-    if "k_fused" in name:
-        m = re.match(r"void fos::k_fused<(\d), (\d), (\d), (\d)>", name)
-        dt, rc, mt, pr = m.groups()
-        err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
+    m = re.match(r"void fos::k_fused<(\d), (\d), (\d), (\d), (\d)>", name)
+    if m:
+        dt, rc, mt, pr, od = m.groups()
+        err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
         return f"fused amax + 1x16 quantize {_DT[dt]} {_RC[rc]}{err} tensor"
+    m = re.match(r"void fos::k_dequant<(\d), (\d)>", name)
+    if m:
+        dt, gr = m.groups()
+        return f"dequantize to {_DT[dt]} {_GR[gr]}"
+    if "k_amax_tensor" in name:
+        return "amax per tensor (" + _DT.get(name.split("<")[1][0], "?") + ")"
     if "k_zero_u32" in name:
         return "clear the amax word"
     if "copyBuffer" in name:
