@@ -154,6 +154,48 @@ def test_specials_match_exact_model(orc):
                 np.testing.assert_array_equal(ge[~np.isnan(ge)], errs[~np.isnan(errs)])
 
 
+def _order_sensitive_blocks(c: int, n_want: int = 4):
+    """Block amaxes a and global amaxes A (bound 448) for which the block
+    scale t = RN(RN(a / c) * S_enc) of R-4 and the other association
+    a * RN(S_enc / c) round to different E4M3 codes: a is placed a few ulps
+    from a midpoint between two E4M3 values, scaled by S_enc. Returns a list
+    of (a, A)."""
+    rng = np.random.default_rng(100 + c)
+    vals = torch.arange(0, 0x7F, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = (vals[1:] + vals[:-1]) / 2
+    A = rng.uniform(1.0, 1000.0, 20000).astype(np.float32)
+    S = (np.float32(2688.0) / A).astype(np.float32)
+    m = mids[rng.integers(8, mids.size, A.size)]
+    a0 = (m * c / S.astype(np.float64)).astype(np.float32)
+    out = []
+    for k in range(-4, 5):
+        a = (a0.view(np.int32) + k).view(np.float32)
+        t1 = ((a / np.float32(c)).astype(np.float32) * S).astype(np.float32)
+        t2 = (a * (S / np.float32(c)).astype(np.float32)).astype(np.float32)
+        e1 = torch.from_numpy(np.minimum(t1, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        e2 = torch.from_numpy(np.minimum(t2, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        for i in np.nonzero((e1 != e2) & (a <= A))[0]:
+            out.append((float(a[i]), float(A[i])))
+    assert len(out) >= n_want, "no order-sensitive blocks found"
+    return out[:n_want]
+
+
+def test_block_scale_rounding_order(orc):
+    """R-4 pinned where it matters: on blocks whose map-to-6 scale depends on
+    the association of RN(a / 6) * S_enc, the oracle's scale equals the exact
+    model's (which takes t = RN(RN(a / 6) * S_enc)). For the map-to-4
+    candidate both associations agree: division by 4 is exact."""
+    c, recipe = 6, "nvfp4"
+    for a, A in _order_sensitive_blocks(c):
+        row = np.array([a] + [a * 0.5 ** (i % 7 + 1) for i in range(15)], np.float32).reshape(1, 16)
+        amax = np.array([A], np.float32)
+        got = orc.quantize(row, "fp32", amax, recipe=recipe)
+        codes, scales, _, _ = exact_model.quantize_tensor(row.astype(np.float64), amax, "1x16", "tensor", 448,
+                                                          recipe, "mse", "exact")
+        np.testing.assert_array_equal(got["scales"], scales, err_msg=f"a={a!r} A={A!r}")
+        np.testing.assert_array_equal(got["codes"], codes)
+
+
 def test_exact_model_rounding_sanity():
     # the model's own binary32 rounding against numpy's float32 cast on random rationals
     rng = np.random.default_rng(1)
