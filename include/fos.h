@@ -197,6 +197,22 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
                          const float* group_amax, const fos_config* cfg, uint8_t* codes, uint8_t* scales,
                          float* group_sdec_out, int32_t* d_status, void* stream);
 
+/* Columnwise quantize: the quantize of X^T (the [K, M] transpose of x,
+ * the operand of the backward GEMM; pytorch/ao PR, recipe commit, and the
+ * Megatron-LM PR's "Limitations and pending work" name the columnwise
+ * output), without materialising X^T. 1x16 blocks run down the columns of
+ * x: block (c, b) holds x[16b .. 16b+15, c]. Outputs are laid out as
+ * fos_quantize of X^T would write them:
+ *   codes_t:  [K, M/2]   (row c: the column c of x, element 2j in the low nibble)
+ *   scales_t: [K, M/16]
+ * Bitwise equal to fos_quantize(transpose(x)) with the same config. Needs
+ * M % 16 == 0, K % 16 == 0, K <= 2^24 and M <= 2^23; cfg must be 1x16 with a
+ * per-tensor amax [1] (the same global scale as the row-wise operand).
+ *   sdec_out: nullable device float[1]. */
+int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, const float* amax,
+                            const fos_config* cfg, uint8_t* codes_t, uint8_t* scales_t, float* sdec_out,
+                            void* stream);
+
 /* Per-tensor amax and quantize in one launch: the amax pre-pass that the
  * Megatron-LM PR runs as a separate FP32 torch reduction ("What does this PR
  * do?", fused data path) folded into the quantizer of the pytorch/ao PR

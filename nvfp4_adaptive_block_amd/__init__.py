@@ -64,6 +64,7 @@ _SIGS = {
     "nvfp4_dequantize": (_I, [_P, _P, _I64, _I64, _P, _I, _I, _P, _P]),
     "fos_quantize_grouped": (_I, [_P, _I, _I64, _I64, _P, _I, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_quantize_fused": (_I, [_P, _I, _I64, _I64, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P, _P]),
+    "fos_quantize_columnwise": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -183,6 +184,25 @@ def fos_quantize_fused(x: torch.Tensor, *, codes=None, scales=None, amax=None, s
                                                  _ptr(scales), _ptr(amax), _ptr(sdec), _ptr(workspace),
                                                  _ptr(status), _stream(dev)))
     return codes, scales, amax, sdec
+
+
+def fos_quantize_columnwise(x: torch.Tensor, amax: torch.Tensor, *, codes=None, scales=None, sdec=None, **knobs):
+    """Quantize the transpose of x[M, K] without materialising it. Returns
+    (codes uint8[K, M/2], scales uint8[K, M/16], sdec float32[1])."""
+    _need(x, "x")
+    M, K = x.shape
+    cfg = config(**knobs)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(K, M // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(K, M // 16, dtype=torch.uint8, device=dev)
+    if sdec is None:
+        sdec = torch.empty(1, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().fos_quantize_columnwise(_ptr(x), DTYPES[x.dtype], M, K, _ptr(amax), ctypes.byref(cfg),
+                                                      _ptr(codes), _ptr(scales), _ptr(sdec), _stream(dev)))
+    return codes, scales, sdec
 
 
 def fos_qdq(x: torch.Tensor, amax: torch.Tensor, *, out=None, **knobs) -> torch.Tensor:

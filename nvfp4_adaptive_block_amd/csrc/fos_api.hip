@@ -321,6 +321,37 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
   return launch_status(fos::launch_quant_1x16(dtype, cfg->recipe, metric, prec, order, fos::kGranGroup, a, s));
 }
 
+int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, const float* amax,
+                            const fos_config* cfg, uint8_t* codes_t, uint8_t* scales_t, float* sdec_out,
+                            void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
+    return fail(FOS_ERR_CONFIG, "columnwise quantize supports 1x16 blocks with a per-tensor amax");
+  if ((rc = check_shape(M, K, FOS_BLOCK_16X16))) return rc;  // M % 16, K % 16, K <= 2^24
+  if (M > (int64_t(1) << 23)) return fail(FOS_ERR_SHAPE, "columnwise quantize needs M <= 2^23, M=%lld", (long long)M);
+  if (!amax) return fail(FOS_ERR_INVALID_ARG, "amax is NULL");
+  if (M * K > 0 && (!x || !codes_t || !scales_t)) return fail(FOS_ERR_INVALID_ARG, "x, codes_t and scales_t must be non-NULL");
+  if (!aligned(x, 16) || !aligned(codes_t, 8)) return fail(FOS_ERR_ALIGN, "x or codes_t misaligned");
+  if (!aligned(amax, 4) || !aligned(sdec_out, 4)) return fail(FOS_ERR_ALIGN, "amax/sdec misaligned");
+  if ((rc = check_device())) return rc;
+  if (M * K == 0 && !sdec_out) return FOS_OK;
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
+  fos::Args16x16 a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.amax = amax;
+  a.M = M;
+  a.K = K;
+  a.six_b = six_b(cfg);
+  a.codes = codes_t;
+  a.scales = scales_t;
+  a.sdec_out = sdec_out;
+  return launch_status(fos::launch_colwise(dtype, cfg->recipe, metric, prec, order, a, static_cast<hipStream_t>(stream)));
+}
+
 int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
                        uint8_t* scales, float* amax_out, float* sdec_out, void* workspace, int32_t* d_status,
                        void* stream) {

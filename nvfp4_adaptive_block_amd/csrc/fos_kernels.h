@@ -77,6 +77,7 @@ hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, con
                         float* amax_out, hipStream_t s);
 hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, int gran,
                            const Args1x16<kMaxList>& a, hipStream_t s);
+hipError_t launch_colwise(int dt, int recipe, int metric, int prec, int order, const Args16x16& a, hipStream_t s);
 hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int out, const Args16x16& a,
                         hipStream_t s);
 hipError_t launch_dequant(int dt, int gran, const uint8_t* codes, const uint8_t* scales, const float* sdec,

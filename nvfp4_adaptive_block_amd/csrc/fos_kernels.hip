@@ -858,6 +858,85 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   }
 }
 
+// ------------------------------------------------------------ columnwise
+
+// Columnwise quantize: the 1x16 quantize of X^T ([K, M]), whose blocks are
+// 16 consecutive rows of one column of X (the transposed operand of the
+// backward GEMM). A lane reads 16 bytes of each of a band's 16 rows: kCols
+// columns (8 for 16-bit inputs, 4 for fp32), so each load instruction covers
+// 1 KiB of one row, and each of the lane's columns is one block of X^T held
+// in the lane's registers. A unit is one 16-row band of a strip of 64 kCols
+// columns; a wave walks down the bands of its strip, so its consecutive
+// stores fill adjacent bytes of the same rows of X^T.
+template <int DT> struct ColW {
+  static constexpr int kCols = (DT == kFP32) ? 4 : 8;  // columns per lane
+  static constexpr int kW = 64 * kCols;                 // columns per strip
+};
+
+template <int DT>
+__device__ __forceinline__ float col_elem(const v4i& r, int k) {
+  const uint32_t w = (uint32_t)r[DT == kFP32 ? k : (k >> 1)];
+  if (DT == kFP32) return __uint_as_float(w);
+  if (DT == kBF16) return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+  return (k & 1) ? f16_hi(w) : f16_lo(w);
+}
+
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
+__global__ void __launch_bounds__(256) k_colwise(const Args16x16 args) {
+  __shared__ float lds[4][256];
+  constexpr int kEB = Raw<DT>::kBytes / 16;  // bytes per element
+  constexpr int kCols = ColW<DT>::kCols, kW = ColW<DT>::kW;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  const int64_t M = args.M, K = args.K;
+  const int64_t nbands = M >> 4, nstrips = (K + kW - 1) / kW;
+  const int64_t total = nbands * nstrips;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (total + nwaves - 1) / nwaves;
+  int64_t u = wave * per;
+  const int64_t u_end = min(total, u + per);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && args.sdec_out)
+    args.sdec_out[0] = 1.0f / global_encode_scale(args.amax[0], args.six_b);
+  if (u >= u_end) return;
+
+  const float S_enc = global_encode_scale(ld_const(args.amax, 0), args.six_b);
+  const float S_dec = 1.0f / S_enc;
+  tab.build(S_enc, S_dec, lane);
+  const int64_t x_bytes = M * K * kEB, c_bytes = K * (M >> 1), s_bytes = K * (M >> 4);
+  const uint32_t ox = (uint32_t)(lane * 16), ox_row = (uint32_t)(K * kEB);
+  const uint32_t oc_col = (uint32_t)(M >> 1), os_col = (uint32_t)(M >> 4);
+
+  int64_t strip = u / nbands, band = u - strip * nbands;
+  for (; u < u_end; u++) {
+    const int64_t col0 = strip * kW;
+    const bool active = col0 + lane * kCols < K;
+    const int64_t ex = band * 16 * K + col0;             // first element of the unit
+    const int64_t ec = col0 * (M >> 1) + band * 8;        // its first code byte
+    const int64_t es = col0 * (M >> 4) + band;            // its first scale byte
+    const Rsrc rx = make_rsrc(static_cast<const char*>(args.x) + ex * kEB, x_bytes - ex * kEB);
+    const Rsrc rc = make_rsrc(args.codes + ec, c_bytes - ec);
+    const Rsrc rs = make_rsrc(args.scales + es, s_bytes - es);
+    v4i rows[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      rows[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, active ? ox + r * ox_row : kOOB, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kCols; k++) {
+      float x[16], xh[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) x[r] = col_elem<DT>(rows[r], k);
+      BlockOut o;
+      quantize_block<RECIPE, METRIC, PREC, ORDER, false, true>(x, S_enc, S_dec, tab, o, xh);
+      const uint32_t col = (uint32_t)(lane * kCols + k);
+      store_codes(rc, active ? col * oc_col : kOOB, o.c0, o.c1);
+      store_scale(rs, active ? col * os_col : kOOB, o.scale);
+    }
+    if (++band == nbands) { band = 0; ++strip; }
+  }
+}
+
 // ------------------------------------------------------------ dequantize
 
 // Plain global stores of 16 decoded values as the output type.
@@ -1256,6 +1335,18 @@ static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
+static hipError_t launch_colwise_t(const Args16x16& a, hipStream_t s) {
+  static_assert(GRAN == kGranTensor && OUT == kOutQuant, "columnwise: per-tensor quantize only");
+  auto* fn = &k_colwise<DT, RECIPE, METRIC, PREC, ORDER>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  constexpr int64_t kW = ColW<DT>::kW;
+  const int64_t units = (a.M / 16) * ((a.K + kW - 1) / kW);
+  const int64_t grid = max((int64_t)1, min(resident, (units + 3) / 4));
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DT, int RECIPE, int METRIC, int PREC, int GRAN, int OUT>
 static hipError_t launch_16x16_t(const Args16x16& a, hipStream_t s) {
   auto* fn = &k_16x16<DT, RECIPE, METRIC, PREC, GRAN, OUT>;
@@ -1317,6 +1408,12 @@ hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, 
                            const Args1x16<kMaxList>& a, hipStream_t s) {
   if (gran == kGranTensor) { FOS_DTYPES(FOS_MODES, kGranTensor, kOutQdq, CALL_QL) }
   FOS_DTYPES(FOS_MODES, kGranRow, kOutQdq, CALL_QL)
+}
+
+#define CALL_C(DT, R, M, P, O, G, OUT) launch_colwise_t<DT, R, M, P, O, G, OUT>(a, s)
+
+hipError_t launch_colwise(int dt, int recipe, int metric, int prec, int order, const Args16x16& a, hipStream_t s) {
+  FOS_DTYPES(FOS_MODES, kGranTensor, kOutQuant, CALL_C)
 }
 
 hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int out, const Args16x16& a,

@@ -194,3 +194,23 @@ def test_dequantize_8192x4096(orc, out_dtype, gran):
     got = raw_bits(y.cpu())[rows]
     view = np.uint32 if out_dtype == "fp32" else np.uint16
     np.testing.assert_array_equal(np.ascontiguousarray(got).view(view), np.ascontiguousarray(want).view(view))
+
+
+def test_columnwise_dense_activation_8192x4096(orc):
+    """The transposed operand of the dense activation tensor at full size:
+    sampled columns of x (rows of x^T) against the oracle's quantize of the
+    transpose, every mode."""
+    M, K = 8192, 4096
+    x = synthdata.activation_family("outlier", M, K, 23, "bf16")
+    bits = raw_bits(x)
+    a = orc.amax(bits, "bf16", "tensor")
+    cols = sample_rows(K, 48, 77)
+    xt_rows = np.ascontiguousarray(bits[:, cols].T)
+    xd = x.to("cuda")
+    for (recipe, metric, prec), bound in itertools.product(MODES, BOUNDS):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+        codes, scales, _ = fos.fos_quantize_columnwise(xd, torch.from_numpy(a).to("cuda"), **kw)
+        torch.cuda.synchronize()
+        want = orc.quantize(xt_rows, "bf16", a, **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[cols], want["scales"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[cols], want["codes"], err_msg=f"{kw}")

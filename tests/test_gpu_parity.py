@@ -434,3 +434,32 @@ def test_qdq_every_dtype_block_and_granularity(orc, dtype, block, gran):
             np.testing.assert_array_equal(u_bits(bits_of(ys[i])), u_bits(orc.qdq(bs[i], dtype, ams[i], **kw)),
                                           err_msg=f"{i} {kw}")
         np.testing.assert_array_equal(u_bits(bits_of(y0)), u_bits(orc.qdq(bs[0], dtype, ams[0], **kw)))
+
+
+# ------------------------------------------------------------------ columnwise
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("shape,family", [((48, 272), "outlier"), ((16, 16), "special"), ((96, 1040), "normal"),
+                                          ((32, 4096), "special"), ((272, 48), "weight")])
+def test_columnwise_is_quantize_of_the_transpose(orc, dtype, shape, family):
+    """fos_quantize_columnwise(x) equals the oracle's quantize of x^T, every
+    mode, both bounds and both error orders; ragged column strips."""
+    M, K = shape
+    x = _family(family, dtype, M, K, 73)
+    if family == "special":
+        x = x.to(torch.float32)
+        x[3, 5] = float("nan")
+        x[7, 9] = float("-inf")
+        x = x.to(synthdata.TORCH_DTYPES[dtype])
+    b = raw_bits(x)
+    bt = np.ascontiguousarray(b.T)
+    a = orc.amax(b, dtype, "tensor")
+    modes = [(r, m, p, o) for (r, m, p) in MODES for o in (("tree", "seq") if r == "4over6" else ("tree",))]
+    for (recipe, metric, prec, order), bound in itertools.product(modes, (448, 256)):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, err_order=order)
+        codes, scales, sdec = fos.fos_quantize_columnwise(dev(x), dev(torch.from_numpy(a)), **kw)
+        torch.cuda.synchronize()
+        want = orc.quantize(bt, dtype, a, **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{shape} {kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{shape} {kw}")
+        np.testing.assert_array_equal(sdec.cpu().numpy().view(np.uint32), want["sdec"].view(np.uint32))
