@@ -862,78 +862,106 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
 
 // Columnwise quantize: the 1x16 quantize of X^T ([K, M]), whose blocks are
 // 16 consecutive rows of one column of X (the transposed operand of the
-// backward GEMM). A lane reads 16 bytes of each of a band's 16 rows: kCols
-// columns (8 for 16-bit inputs, 4 for fp32), so each load instruction covers
-// 1 KiB of one row, and each of the lane's columns is one block of X^T held
-// in the lane's registers. A unit is one 16-row band of a strip of 64 kCols
-// columns; a wave walks down the bands of its strip, so its consecutive
-// stores fill adjacent bytes of the same rows of X^T.
-template <int DT> struct ColW {
-  static constexpr int kCols = (DT == kFP32) ? 4 : 8;  // columns per lane
-  static constexpr int kW = 64 * kCols;                 // columns per strip
-};
+// backward GEMM).
+//
+// A workgroup's unit is a tile of 16 bands (256 rows) by 256 columns. Each
+// of its four waves quantizes four of the bands: a lane reads 4 columns of
+// each of the band's 16 rows (one 8- or 16-byte load per row, 512 B or
+// 1 KiB per load instruction) and each of those columns is one block of X^T
+// in the lane's registers. The codes and scales go to LDS ([band][slot],
+// where column c = 4 j + k of lane j sits in slot 64 k + j, so that a
+// wave's LDS writes are consecutive; rows padded by one element); after a
+// barrier the
+// workgroup writes each column's 16 bands as one 128-byte run of its X^T
+// code row (and 16 bytes of its scale row), so X^T rows are written in
+// whole lines rather than 8-byte pieces from different waves.
+constexpr int kColT = 256;   // columns per tile
+constexpr int kColCL = 4;    // columns per lane
 
 template <int DT>
-__device__ __forceinline__ float col_elem(const v4i& r, int k) {
-  const uint32_t w = (uint32_t)r[DT == kFP32 ? k : (k >> 1)];
-  if (DT == kFP32) return __uint_as_float(w);
-  if (DT == kBF16) return (k & 1) ? bf16_hi(w) : bf16_lo(w);
-  return (k & 1) ? f16_hi(w) : f16_lo(w);
+__device__ __forceinline__ float col_elem(const uint32_t* w, int k) {
+  if (DT == kFP32) return __uint_as_float(w[k]);
+  const uint32_t v = w[k >> 1];
+  if (DT == kBF16) return (k & 1) ? bf16_hi(v) : bf16_lo(v);
+  return (k & 1) ? f16_hi(v) : f16_lo(v);
 }
 
 template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
 __global__ void __launch_bounds__(256) k_colwise(const Args16x16 args) {
-  __shared__ float lds[4][256];
+  __shared__ float lds_tab[4][256];
+  __shared__ uint64_t lds_codes[16][kColT + 1];
+  __shared__ uint8_t lds_scales[16][kColT + 4];
   constexpr int kEB = Raw<DT>::kBytes / 16;  // bytes per element
-  constexpr int kCols = ColW<DT>::kCols, kW = ColW<DT>::kW;
+  constexpr int kW = kColCL * kEB / 4;       // 32-bit words a lane loads per row
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const Table tab{lds[wv], lds[wv] + 128};
+  const Table tab{lds_tab[wv], lds_tab[wv] + 128};
   const int64_t M = args.M, K = args.K;
-  const int64_t nbands = M >> 4, nstrips = (K + kW - 1) / kW;
-  const int64_t total = nbands * nstrips;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (total + nwaves - 1) / nwaves;
-  int64_t u = wave * per;
-  const int64_t u_end = min(total, u + per);
+  const int64_t nbands = M >> 4;
+  const int64_t ngroups = (nbands + 15) >> 4, nstrips = (K + kColT - 1) / kColT;
+  const int64_t total = ngroups * nstrips;
   if (blockIdx.x == 0 && threadIdx.x == 0 && args.sdec_out)
     args.sdec_out[0] = 1.0f / global_encode_scale(args.amax[0], args.six_b);
-  if (u >= u_end) return;
+  if ((int64_t)blockIdx.x >= total) return;
 
   const float S_enc = global_encode_scale(ld_const(args.amax, 0), args.six_b);
   const float S_dec = 1.0f / S_enc;
   tab.build(S_enc, S_dec, lane);
   const int64_t x_bytes = M * K * kEB, c_bytes = K * (M >> 1), s_bytes = K * (M >> 4);
-  const uint32_t ox = (uint32_t)(lane * 16), ox_row = (uint32_t)(K * kEB);
-  const uint32_t oc_col = (uint32_t)(M >> 1), os_col = (uint32_t)(M >> 4);
+  const uint32_t row_bytes = (uint32_t)(K * kEB);
 
-  int64_t strip = u / nbands, band = u - strip * nbands;
-  for (; u < u_end; u++) {
-    const int64_t col0 = strip * kW;
-    const bool active = col0 + lane * kCols < K;
-    const int64_t ex = band * 16 * K + col0;             // first element of the unit
-    const int64_t ec = col0 * (M >> 1) + band * 8;        // its first code byte
-    const int64_t es = col0 * (M >> 4) + band;            // its first scale byte
-    const Rsrc rx = make_rsrc(static_cast<const char*>(args.x) + ex * kEB, x_bytes - ex * kEB);
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int64_t strip = u / ngroups, group = u - strip * ngroups;
+    const int64_t col0 = strip * kColT;
+    const bool col_ok = col0 + lane * kColCL < K;
+    // quantize four bands of the tile (band 4 i + wave of the group)
+#pragma unroll 1
+    for (int i = 0; i < 4; i++) {
+      const int bg = 4 * i + wv;                 // band within the group
+      const int64_t band = group * 16 + bg;
+      const bool band_ok = band < nbands;        // wave-uniform
+      const int64_t ex = band * 16 * K + col0;   // first element of the wave's rows
+      const Rsrc rx = make_rsrc(static_cast<const char*>(args.x) + (band_ok ? ex : 0) * kEB,
+                                band_ok ? x_bytes - ex * kEB : 0);
+      uint32_t w[16][kW];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const uint32_t off = col_ok ? r * row_bytes + lane * kColCL * kEB : kOOB;
+        if (kW == 2) {
+          const v2i v = (v2i)__builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+          w[r][0] = (uint32_t)v.x; w[r][1] = (uint32_t)v.y;
+        } else {
+          const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+          w[r][0] = (uint32_t)v.x; w[r][1] = (uint32_t)v.y; w[r][2] = (uint32_t)v.z; w[r][3] = (uint32_t)v.w;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kColCL; k++) {
+        float x[16], xh[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) x[r] = col_elem<DT>(w[r], k);
+        BlockOut o;
+        quantize_block<RECIPE, METRIC, PREC, ORDER, false, true>(x, S_enc, S_dec, tab, o, xh);
+        lds_codes[bg][64 * k + lane] = (uint64_t)o.c0 | ((uint64_t)o.c1 << 32);
+        lds_scales[bg][64 * k + lane] = (uint8_t)o.scale;
+      }
+    }
+    __syncthreads();
+    // write out: element e = column * 16 + band of the tile, so a wave's
+    // 64 lanes cover 4 columns x 16 bands (4 whole 128-byte code runs)
+    const int64_t ec = col0 * (M >> 1) + group * 128;  // code byte of (col0, band 16 group)
+    const int64_t es = col0 * (M >> 4) + group * 16;
     const Rsrc rc = make_rsrc(args.codes + ec, c_bytes - ec);
     const Rsrc rs = make_rsrc(args.scales + es, s_bytes - es);
-    v4i rows[16];
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-      rows[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, active ? ox + r * ox_row : kOOB, 0, 0);
-#pragma unroll
-    for (int k = 0; k < kCols; k++) {
-      float x[16], xh[16];
-#pragma unroll
-      for (int r = 0; r < 16; r++) x[r] = col_elem<DT>(rows[r], k);
-      BlockOut o;
-      quantize_block<RECIPE, METRIC, PREC, ORDER, false, true>(x, S_enc, S_dec, tab, o, xh);
-      const uint32_t col = (uint32_t)(lane * kCols + k);
-      store_codes(rc, active ? col * oc_col : kOOB, o.c0, o.c1);
-      store_scale(rs, active ? col * os_col : kOOB, o.scale);
+#pragma unroll 4
+    for (int e = threadIdx.x; e < kColT * 16; e += 256) {
+      const int col = e >> 4, bg = e & 15, slot = 64 * (col & 3) + (col >> 2);
+      const bool ok = col0 + col < K && group * 16 + bg < nbands;
+      const uint64_t c = lds_codes[bg][slot];
+      store_codes(rc, ok ? (uint32_t)(col * (M >> 1) + bg * 8) : kOOB, (uint32_t)c, (uint32_t)(c >> 32));
+      store_scale(rs, ok ? (uint32_t)(col * (M >> 4) + bg) : kOOB, lds_scales[bg][slot]);
     }
-    if (++band == nbands) { band = 0; ++strip; }
+    __syncthreads();
   }
 }
 
@@ -1340,9 +1368,8 @@ static hipError_t launch_colwise_t(const Args16x16& a, hipStream_t s) {
   static_assert(GRAN == kGranTensor && OUT == kOutQuant, "columnwise: per-tensor quantize only");
   auto* fn = &k_colwise<DT, RECIPE, METRIC, PREC, ORDER>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
-  constexpr int64_t kW = ColW<DT>::kW;
-  const int64_t units = (a.M / 16) * ((a.K + kW - 1) / kW);
-  const int64_t grid = max((int64_t)1, min(resident, (units + 3) / 4));
+  const int64_t tiles = ((a.M / 16 + 15) / 16) * ((a.K + kColT - 1) / kColT);
+  const int64_t grid = max((int64_t)1, min(resident, tiles));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
