@@ -864,45 +864,51 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
 // 16 consecutive rows of one column of X (the transposed operand of the
 // backward GEMM).
 //
-// A workgroup's unit is a tile of 16 bands (256 rows) by 256 columns. Each
-// of its four waves quantizes four of the bands: a lane reads 4 columns of
-// each of the band's 16 rows (one 8- or 16-byte load per row, 512 B or
-// 1 KiB per load instruction) and each of those columns is one block of X^T
-// in the lane's registers. The codes and scales go to LDS ([band][slot],
-// where column c = 4 j + k of lane j sits in slot 64 k + j, so that a
-// wave's LDS writes are consecutive; rows padded by one element); after a
-// barrier the
-// workgroup writes each column's 16 bands as one 128-byte run of its X^T
-// code row (and 16 bytes of its scale row), so X^T rows are written in
-// whole lines rather than 8-byte pieces from different waves.
-constexpr int kColT = 256;   // columns per tile
-constexpr int kColCL = 4;    // columns per lane
+// A wave's unit is a tile of 16 bands (256 rows) by 64 columns, and lane j
+// owns column j of it: for each band the lane loads its column's 16 values
+// (one 2- or 4-byte load per row, so one load instruction is 128 or 256
+// contiguous bytes of one row), quantizes that block, and keeps its codes in
+// a wave-private LDS area and its scales in a four-register shift queue. The
+// next band's rows load while the current band is quantized. When the tile
+// is done the lane holds its column's whole 128-byte run of X^T codes and
+// 16 scale bytes; the wave writes the runs eight columns per store
+// instruction (16 bytes per lane, whole 128-byte lines), so no X^T line is
+// assembled from pieces written by different waves. Waves never wait for
+// one another.
+//
+// The scale runs (16 bytes per column per tile) fill an X^T scale line
+// together with the seven neighbouring tiles of the same column strip. The
+// tile order is arranged so that those eight tiles run on one XCD (whose
+// L2 then merges the pieces): workgroup b runs on XCD b % 8, and the tiles
+// are dealt out as if the workgroups of one XCD were consecutive.
+constexpr int kColTW = 64;  // columns per wave tile
 
 template <int DT>
-__device__ __forceinline__ float col_elem(const uint32_t* w, int k) {
-  if (DT == kFP32) return __uint_as_float(w[k]);
-  const uint32_t v = w[k >> 1];
-  if (DT == kBF16) return (k & 1) ? bf16_hi(v) : bf16_lo(v);
-  return (k & 1) ? f16_hi(v) : f16_lo(v);
+__device__ __forceinline__ float col_value(uint32_t w) {
+  if (DT == kFP32) return __uint_as_float(w);
+  if (DT == kBF16) return __uint_as_float(w << 16);
+  return f16_lo(w);
 }
 
 template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
 __global__ void __launch_bounds__(256) k_colwise(const Args16x16 args) {
   __shared__ float lds_tab[4][256];
-  __shared__ uint64_t lds_codes[16][kColT + 1];
-  __shared__ uint8_t lds_scales[16][kColT + 4];
-  constexpr int kEB = Raw<DT>::kBytes / 16;  // bytes per element
-  constexpr int kW = kColCL * kEB / 4;       // 32-bit words a lane loads per row
+  __shared__ uint64_t lds_codes[4][kColTW][17];  // [wave][column][band], padded
+  constexpr int kEB = Raw<DT>::kBytes / 16;      // bytes per element
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const Table tab{lds_tab[wv], lds_tab[wv] + 128};
+  uint64_t (&cl)[kColTW][17] = lds_codes[wv];
   const int64_t M = args.M, K = args.K;
   const int64_t nbands = M >> 4;
-  const int64_t ngroups = (nbands + 15) >> 4, nstrips = (K + kColT - 1) / kColT;
+  const int64_t ngroups = (nbands + 15) >> 4, nstrips = (K + kColTW - 1) / kColTW;
   const int64_t total = ngroups * nstrips;
+  // XCD-aware order: the grid is a multiple of 8 workgroups
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  const int64_t wave = ((b & 7) * (G >> 3) + (b >> 3)) * 4 + wv, nwaves = G * 4;
   if (blockIdx.x == 0 && threadIdx.x == 0 && args.sdec_out)
     args.sdec_out[0] = 1.0f / global_encode_scale(args.amax[0], args.six_b);
-  if ((int64_t)blockIdx.x >= total) return;
+  if (wave >= total) return;
 
   const float S_enc = global_encode_scale(ld_const(args.amax, 0), args.six_b);
   const float S_dec = 1.0f / S_enc;
@@ -910,58 +916,92 @@ __global__ void __launch_bounds__(256) k_colwise(const Args16x16 args) {
   const int64_t x_bytes = M * K * kEB, c_bytes = K * (M >> 1), s_bytes = K * (M >> 4);
   const uint32_t row_bytes = (uint32_t)(K * kEB);
 
-  for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
-    const int64_t strip = u / ngroups, group = u - strip * ngroups;
-    const int64_t col0 = strip * kColT;
-    const bool col_ok = col0 + lane * kColCL < K;
-    // quantize four bands of the tile (band 4 i + wave of the group)
-#pragma unroll 1
-    for (int i = 0; i < 4; i++) {
-      const int bg = 4 * i + wv;                 // band within the group
-      const int64_t band = group * 16 + bg;
-      const bool band_ok = band < nbands;        // wave-uniform
-      const int64_t ex = band * 16 * K + col0;   // first element of the wave's rows
-      const Rsrc rx = make_rsrc(static_cast<const char*>(args.x) + (band_ok ? ex : 0) * kEB,
-                                band_ok ? x_bytes - ex * kEB : 0);
-      uint32_t w[16][kW];
+  // Load the lane's 16 values of band bg of tile t (zeros past the tensor).
+  auto load_band = [&](int64_t t, int bg, uint32_t (&w)[16]) {
+    const int64_t strip = t / ngroups, group = t - strip * ngroups;
+    const int64_t band = group * 16 + bg;
+    const bool band_ok = t < total && band < nbands;  // wave-uniform
+    const int64_t ex = band * 16 * K + strip * kColTW;  // first element of the band's rows in the tile
+    const Rsrc rx = make_rsrc(static_cast<const char*>(args.x) + (band_ok ? ex : 0) * kEB,
+                              band_ok ? x_bytes - ex * kEB : 0);
+    // columns past K: an offset past the resource (kOOB + 15 rows < 2^32)
+    const uint32_t lo = strip * kColTW + lane < K ? (uint32_t)(lane * kEB) : kOOB;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const uint32_t off = col_ok ? r * row_bytes + lane * kColCL * kEB : kOOB;
-        if (kW == 2) {
-          const v2i v = (v2i)__builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
-          w[r][0] = (uint32_t)v.x; w[r][1] = (uint32_t)v.y;
-        } else {
-          const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-          w[r][0] = (uint32_t)v.x; w[r][1] = (uint32_t)v.y; w[r][2] = (uint32_t)v.z; w[r][3] = (uint32_t)v.w;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kColCL; k++) {
-        float x[16], xh[16];
-#pragma unroll
-        for (int r = 0; r < 16; r++) x[r] = col_elem<DT>(w[r], k);
-        BlockOut o;
-        quantize_block<RECIPE, METRIC, PREC, ORDER, false, true>(x, S_enc, S_dec, tab, o, xh);
-        lds_codes[bg][64 * k + lane] = (uint64_t)o.c0 | ((uint64_t)o.c1 << 32);
-        lds_scales[bg][64 * k + lane] = (uint8_t)o.scale;
-      }
+    for (int r = 0; r < 16; r++) {
+      if (DT == kFP32) w[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rx, lo + r * row_bytes, 0, 0);
+      else w[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, lo + r * row_bytes, 0, 0);
     }
-    __syncthreads();
-    // write out: element e = column * 16 + band of the tile, so a wave's
-    // 64 lanes cover 4 columns x 16 bands (4 whole 128-byte code runs)
-    const int64_t ec = col0 * (M >> 1) + group * 128;  // code byte of (col0, band 16 group)
-    const int64_t es = col0 * (M >> 4) + group * 16;
+  };
+
+  uint32_t cur[16], nxt[16];
+  load_band(wave, 0, cur);
+  for (int64_t t = wave; t < total; t += nwaves) {
+    const int64_t strip = t / ngroups, group = t - strip * ngroups;
+    uint32_t sq[4] = {0u, 0u, 0u, 0u};  // scale bytes, band 0 ends in the low byte of sq[0]
+#pragma unroll 1
+    for (int bg = 0; bg < 16; bg++) {
+      if (bg < 15) load_band(t, bg + 1, nxt);
+      else load_band(t + nwaves, 0, nxt);
+      float x[16], xh[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) x[r] = col_value<DT>(cur[r]);
+      BlockOut o;
+      quantize_block<RECIPE, METRIC, PREC, ORDER, false, true>(x, S_enc, S_dec, tab, o, xh);
+      cl[lane][bg] = (uint64_t)o.c0 | ((uint64_t)o.c1 << 32);
+      sq[0] = __builtin_amdgcn_alignbit(sq[1], sq[0], 8);
+      sq[1] = __builtin_amdgcn_alignbit(sq[2], sq[1], 8);
+      sq[2] = __builtin_amdgcn_alignbit(sq[3], sq[2], 8);
+      sq[3] = __builtin_amdgcn_alignbit(o.scale, sq[3], 8);
+#pragma unroll
+      for (int r = 0; r < 16; r++) cur[r] = nxt[r];
+    }
+    // the lanes of this wave read what other lanes wrote
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const int64_t col0 = strip * kColTW;
+    const int nvalid = (int)min((int64_t)16, nbands - group * 16);  // bands of this tile in the tensor
+    // 16-byte stores where every band is in the tensor and the runs are
+    // 16-byte aligned, else 8-byte code and 1-byte scale stores
+    const bool wide_c = nvalid == 16 && ((M >> 1) & 15) == 0 && ((uintptr_t)args.codes & 15) == 0;
+    const bool wide_s = nvalid == 16 && ((M >> 4) & 15) == 0 && ((uintptr_t)args.scales & 15) == 0;
+    const int64_t ec = col0 * (M >> 1) + group * 128, es = col0 * (M >> 4) + group * 16;
     const Rsrc rc = make_rsrc(args.codes + ec, c_bytes - ec);
     const Rsrc rs = make_rsrc(args.scales + es, s_bytes - es);
-#pragma unroll 4
-    for (int e = threadIdx.x; e < kColT * 16; e += 256) {
-      const int col = e >> 4, bg = e & 15, slot = 64 * (col & 3) + (col >> 2);
-      const bool ok = col0 + col < K && group * 16 + bg < nbands;
-      const uint64_t c = lds_codes[bg][slot];
-      store_codes(rc, ok ? (uint32_t)(col * (M >> 1) + bg * 8) : kOOB, (uint32_t)c, (uint32_t)(c >> 32));
-      store_scale(rs, ok ? (uint32_t)(col * (M >> 4) + bg) : kOOB, lds_scales[bg][slot]);
+    // codes: lane L writes bytes 16 (L % 8) .. +15 of column 8 i + L / 8
+    const int piece = lane & 7;
+#pragma unroll
+    for (int i = 0; i < kColTW / 8; i++) {
+      const int col = 8 * i + (lane >> 3);
+      const bool col_ok = col0 + col < K;
+      const uint64_t c0 = cl[col][2 * piece], c1 = cl[col][2 * piece + 1];
+      const uint32_t off = (uint32_t)(col * (M >> 1) + 16 * piece);
+      if (wide_c) {
+        const v4i v = {(int)(uint32_t)c0, (int)(uint32_t)(c0 >> 32), (int)(uint32_t)c1, (int)(uint32_t)(c1 >> 32)};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, col_ok ? off : kOOB, 0, 0);
+      } else {
+        store_codes(rc, col_ok && 2 * piece < nvalid ? off : kOOB, (uint32_t)c0, (uint32_t)(c0 >> 32));
+        store_codes(rc, col_ok && 2 * piece + 1 < nvalid ? off + 8 : kOOB, (uint32_t)c1, (uint32_t)(c1 >> 32));
+      }
     }
-    __syncthreads();
+    // scales: lane j writes its column's 16 bytes
+    {
+      const bool col_ok = col0 + lane < K;
+      const uint32_t off = (uint32_t)(lane * (M >> 4));
+      if (wide_s) {
+        const v4i v = {(int)sq[0], (int)sq[1], (int)sq[2], (int)sq[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, col_ok ? off : kOOB, 0, 0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; k++)
+          store_scale(rs, col_ok && k < nvalid ? off + k : kOOB, (sq[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+      }
+    }
+    // the next tile's LDS writes come after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -1368,8 +1408,10 @@ static hipError_t launch_colwise_t(const Args16x16& a, hipStream_t s) {
   static_assert(GRAN == kGranTensor && OUT == kOutQuant, "columnwise: per-tensor quantize only");
   auto* fn = &k_colwise<DT, RECIPE, METRIC, PREC, ORDER>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
-  const int64_t tiles = ((a.M / 16 + 15) / 16) * ((a.K + kColT - 1) / kColT);
-  const int64_t grid = max((int64_t)1, min(resident, tiles));
+  // one wave per tile up to the resident grid, in whole groups of 8
+  // workgroups (the kernel's XCD-aware tile order needs a multiple of 8)
+  const int64_t tiles = ((a.M / 16 + 15) / 16) * ((a.K + kColTW - 1) / kColTW);
+  const int64_t grid = 8 * max((int64_t)1, min(resident / 8, (tiles + 31) / 32));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -214,3 +214,20 @@ def test_columnwise_dense_activation_8192x4096(orc):
         want = orc.quantize(xt_rows, "bf16", a, **kw)
         np.testing.assert_array_equal(scales.cpu().numpy()[cols], want["scales"], err_msg=f"{kw}")
         np.testing.assert_array_equal(codes.cpu().numpy()[cols], want["codes"], err_msg=f"{kw}")
+
+
+def test_columnwise_several_tiles_per_wave_16384x8192(orc):
+    """A tensor with more 256x64 tiles than the grid has waves (16384 x 8192
+    bf16: 8192 tiles), so each wave walks several tiles: sampled columns
+    against the oracle's quantize of the transpose."""
+    M, K = 16384, 8192
+    x = synthdata.activation_family("normal", M, K, 29, "bf16")
+    bits = raw_bits(x)
+    a = orc.amax(bits, "bf16", "tensor")
+    cols = sample_rows(K, 40, 78, extra=[63, 64])
+    xt_rows = np.ascontiguousarray(bits[:, cols].T)
+    codes, scales, _ = fos.fos_quantize_columnwise(x.to("cuda"), torch.from_numpy(a).to("cuda"), recipe="4over6")
+    torch.cuda.synchronize()
+    want = orc.quantize(xt_rows, "bf16", a, recipe="4over6")
+    np.testing.assert_array_equal(scales.cpu().numpy()[cols], want["scales"])
+    np.testing.assert_array_equal(codes.cpu().numpy()[cols], want["codes"])

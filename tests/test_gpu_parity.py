@@ -440,10 +440,13 @@ def test_qdq_every_dtype_block_and_granularity(orc, dtype, block, gran):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("shape,family", [((48, 272), "outlier"), ((16, 16), "special"), ((96, 1040), "normal"),
-                                          ((32, 4096), "special"), ((272, 48), "weight")])
+                                          ((32, 4096), "special"), ((272, 48), "weight"), ((512, 208), "normal"),
+                                          ((528, 80), "outlier")])
 def test_columnwise_is_quantize_of_the_transpose(orc, dtype, shape, family):
     """fos_quantize_columnwise(x) equals the oracle's quantize of x^T, every
-    mode, both bounds and both error orders; ragged column strips."""
+    mode, both bounds and both error orders: ragged column strips, a partial
+    last 256-row group (528 rows), whole aligned groups (512 rows, the
+    16-byte store path) and rows that leave the xT runs 8-byte aligned."""
     M, K = shape
     x = _family(family, dtype, M, K, 73)
     if family == "special":
