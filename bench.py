@@ -330,6 +330,16 @@ def describe_kernel(name: str) -> str:
         dt, rc, mt, pr, od = m.groups()
         err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
         return f"fused amax + 1x16 quantize {_DT[dt]} {_RC[rc]}{err} tensor"
+    m = re.match(r"void fos::k_fused_grouped<(\d), (\d), (\d), (\d), (\d)>", name)
+    if m:
+        dt, rc, mt, pr, od = m.groups()
+        err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
+        return f"fused group amaxes + grouped 1x16 quantize {_DT[dt]} {_RC[rc]}{err}"
+    m = re.match(r"void fos::k_colwise<(\d), (\d), (\d), (\d), (\d)>", name)
+    if m:
+        dt, rc, mt, pr, od = m.groups()
+        err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
+        return f"columnwise 1x16 quantize {_DT[dt]} {_RC[rc]}{err} tensor"
     m = re.match(r"void fos::k_dequant<(\d), (\d)>", name)
     if m:
         dt, gr = m.groups()
@@ -470,6 +480,17 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
     out["amax_then_quantize_bf16_8192x4096"] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb + 2 * n, avg)}
     log(f"[bench] fos_amax + fos_quantize (two launches): {avg * 1e3:.1f} us")
 
+    # columnwise quantize (the transpose's codes and scales) of the same tensor
+    ct = torch.empty(xs[0].shape[1], xs[0].shape[0] // 2, dtype=torch.uint8, device="cuda")
+    st = torch.empty(xs[0].shape[1], xs[0].shape[0] // 16, dtype=torch.uint8, device="cuda")
+    _, ms = time_loop(lambda i: fos.fos_quantize_columnwise(xs[i], amax[i], codes=ct, scales=st, sdec=sdec[i],
+                                                            **knobs), len(xs), 200, 10)
+    avg = float(np.median(ms))
+    out["quantize_columnwise_bf16_8192x4096"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
+                                                 "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
+    log(f"[bench] columnwise bf16 8192x4096: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
+    del ct, st
+
     # nvfp4_dequantize of the step's outputs back to bf16 (the dequantized-
     # backward recompute): reads 0.5625 B/elem, writes 2 B/elem
     ys = [torch.empty_like(x) for x in xs]
@@ -540,6 +561,19 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
         out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
                     "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
         log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
+    # the group amaxes and the grouped quantize in one launch: x's data rows
+    # are read twice (amax phase, quantize phase)
+    ga = torch.empty(G, dtype=torch.float32, device="cuda")
+    gs = torch.empty(G, dtype=torch.float32, device="cuda")
+    fbytes = nbytes + M * K * 2
+    _, ms = time_loop(lambda i: fos.fos_quantize_grouped_fused(x, offs_d, codes=c, scales=s, group_amax=ga,
+                                                               group_sdec=gs, recipe="4over6", err_metric="mse",
+                                                               err_prec="exact", bound=448), 1, steps, warmup)
+    avg = float(np.median(ms))
+    key = f"fused_amax_quantize_grouped_{M}+{pad}x{K}_G{G}_448"
+    out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(fbytes, avg),
+                "frac": round(gbs(fbytes, avg) / PEAK_HBM_GBS, 4)}
+    log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(fbytes, avg):.0f} GB/s")
     return out
 
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FOS_ABI_VERSION 2
+#define FOS_ABI_VERSION 3
 
 /* element types */
 #define FOS_BF16 0
@@ -109,10 +109,13 @@ extern "C" {
 /* device status bits */
 #define FOS_STATUS_TILE_NONUNIFORM 1 /* 16x16 with a per-row amax that differs within a 16-row band */
 #define FOS_STATUS_BAD_OFFS 2        /* group offsets not monotone, not multiples of 16, or past M_alloc */
-#define FOS_STATUS_BARRIER_TIMEOUT 4 /* fos_quantize_fused: the grid barrier did not complete (workspace not zero) */
+#define FOS_STATUS_BARRIER_TIMEOUT 4 /* fused calls: the grid barrier did not complete (workspace not zero) */
 
-/* Bytes of the device workspace fos_quantize_fused needs. */
+/* Bytes of the device workspace the fused calls (fos_quantize_fused,
+ * fos_quantize_grouped_fused) need; the most groups the fused grouped call
+ * takes (added in ABI version 3). */
 #define FOS_FUSED_WORKSPACE_BYTES 16384
+#define FOS_FUSED_MAX_GROUPS 256
 
 typedef struct fos_config {
     int32_t recipe;     /* FOS_RECIPE_* */
@@ -240,6 +243,33 @@ int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, cons
 int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
                        uint8_t* scales, float* amax_out, float* sdec_out, void* workspace, int32_t* d_status,
                        void* stream);
+
+/* Grouped (MoE) amax and quantize in one launch: the group amaxes that
+ * fos_quantize_grouped takes as input (pytorch/ao PR, MoE commit; the
+ * Megatron-LM PR's separate amax pre-pass, "What does this PR do?") are
+ * computed in the same launch. Group g's amax is the NaN-dropping max |x|
+ * over rows [offs[g-1], offs[g]) (0 for an empty group); padding rows at or
+ * past offs[G-1] are neither read nor counted. The result equals fos_amax of
+ * each group slice followed by fos_quantize_grouped with those amaxes, bit
+ * for bit. cfg must be 1x16; cfg->scale_gran is ignored. 1 <= G <=
+ * FOS_FUSED_MAX_GROUPS.
+ *   offs:           device int32[G], as for fos_quantize_grouped.
+ *   group_amax_out: nullable device float[G], receives the group amaxes.
+ *   group_sdec_out: nullable device float[G], receives each group's S_dec.
+ *   workspace:      as for fos_quantize_fused: FOS_FUSED_WORKSPACE_BYTES,
+ *                   zero before its first use, one per stream that may
+ *                   overlap. Fused per-tensor and fused grouped calls may
+ *                   share it. Grouped calls also keep a call counter and
+ *                   two banks of group maxima in it (they alternate; each
+ *                   call clears the bank the next one uses).
+ *   d_status:       nullable device int32: FOS_STATUS_BAD_OFFS as for
+ *                   fos_quantize_grouped, FOS_STATUS_BARRIER_TIMEOUT as for
+ *                   fos_quantize_fused.
+ * After FOS_STATUS_BARRIER_TIMEOUT from either fused call, clear the
+ * workspace to zero again before its next use. */
+int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                               const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
+                               float* group_sdec_out, void* workspace, int32_t* d_status, void* stream);
 
 #ifdef __cplusplus
 }

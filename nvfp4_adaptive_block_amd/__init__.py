@@ -31,6 +31,7 @@ STATUS_TILE_NONUNIFORM = 1
 STATUS_BAD_OFFS = 2
 STATUS_BARRIER_TIMEOUT = 4
 FUSED_WORKSPACE_BYTES = 16384  # FOS_FUSED_WORKSPACE_BYTES
+FUSED_MAX_GROUPS = 256  # FOS_FUSED_MAX_GROUPS
 
 
 class FosError(RuntimeError):
@@ -65,6 +66,8 @@ _SIGS = {
     "fos_quantize_grouped": (_I, [_P, _I, _I64, _I64, _P, _I, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_quantize_fused": (_I, [_P, _I, _I64, _I64, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P, _P]),
     "fos_quantize_columnwise": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P]),
+    "fos_quantize_grouped_fused": (_I, [_P, _I, _I64, _I64, _P, _I, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P,
+                                        _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -152,7 +155,7 @@ _workspaces: dict = {}
 
 
 def fused_workspace(device) -> torch.Tensor:
-    """The zero-initialised workspace fos_quantize_fused uses on `device` when
+    """The zero-initialised workspace the fused calls use on `device` when
     the caller passes none (one per device; calls on one device's streams
     that may overlap need workspaces of their own)."""
     dev = torch.device(device)
@@ -271,3 +274,30 @@ def fos_quantize_grouped(x: torch.Tensor, offs: torch.Tensor, group_amax: torch.
                                                    ctypes.byref(cfg), _ptr(codes), _ptr(scales), _ptr(group_sdec),
                                                    _ptr(status), _stream(dev)))
     return codes, scales, group_sdec
+
+
+def fos_quantize_grouped_fused(x: torch.Tensor, offs: torch.Tensor, *, codes=None, scales=None, group_amax=None,
+                               group_sdec=None, status=None, workspace=None, **knobs):
+    """Group amaxes and the grouped quantize in one launch. Returns (codes,
+    scales, group_amax float32[G], group_sdec float32[G])."""
+    _need(x, "x")
+    M, K = x.shape
+    dev = x.device
+    G = offs.numel()
+    cfg = config(**knobs)
+    if codes is None:
+        codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
+    if group_amax is None:
+        group_amax = torch.empty(G, dtype=torch.float32, device=dev)
+    if group_sdec is None:
+        group_sdec = torch.empty(G, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = fused_workspace(dev)
+    with torch.cuda.device(dev):
+        _check(load_library().fos_quantize_grouped_fused(_ptr(x), DTYPES[x.dtype], M, K, _ptr(offs), G,
+                                                         ctypes.byref(cfg), _ptr(codes), _ptr(scales),
+                                                         _ptr(group_amax), _ptr(group_sdec), _ptr(workspace),
+                                                         _ptr(status), _stream(dev)))
+    return codes, scales, group_amax, group_sdec

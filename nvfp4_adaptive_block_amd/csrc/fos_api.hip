@@ -114,6 +114,7 @@ void mode_of(const fos_config* c, int& metric, int& prec, int& order) {
 }  // namespace
 
 static_assert(FOS_FUSED_WORKSPACE_BYTES == fos::kFusedWorkspaceBytes, "workspace size mismatch");
+static_assert(FOS_FUSED_MAX_GROUPS == fos::kMaxFusedGroups, "group limit mismatch");
 
 extern "C" {
 
@@ -382,6 +383,44 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   a.status = d_status;
   return launch_status(fos::launch_fused(dtype, cfg->recipe, metric, prec, order, a, static_cast<uint32_t*>(workspace),
                                          amax_out, static_cast<hipStream_t>(stream)));
+}
+
+int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                               const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
+                               float* group_sdec_out, void* workspace, int32_t* d_status, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (cfg->block != FOS_BLOCK_1X16) return fail(FOS_ERR_CONFIG, "grouped quantize supports 1x16 blocks");
+  if ((rc = check_shape(M_alloc, K, FOS_BLOCK_1X16))) return rc;
+  if (G <= 0 || G > FOS_FUSED_MAX_GROUPS)
+    return fail(FOS_ERR_INVALID_ARG, "G must be in [1, %d], got %d", FOS_FUSED_MAX_GROUPS, G);
+  if (!offs) return fail(FOS_ERR_INVALID_ARG, "offs must be non-NULL");
+  if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (M_alloc * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned(x, 16) || !aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "x or codes misaligned");
+  if (!aligned(offs, 4) || !aligned(group_amax_out, 4) || !aligned(group_sdec_out, 4) || !aligned(d_status, 4) ||
+      !aligned(workspace, 4))
+    return fail(FOS_ERR_ALIGN, "offs/amax/sdec/status/workspace misaligned");
+  if ((rc = check_device())) return rc;
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
+  fos::Args1x16<1> a;
+  memset(&a, 0, sizeof a);
+  a.t[0] = fos::TensorRef{x, nullptr, nullptr, M_alloc, K > 0 ? K : 16, 0};
+  a.n = 1;
+  a.G = G;
+  const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
+  a.total_units = M_alloc * ((K / 16 + ub - 1) / ub);  // per-row segments
+  a.six_b = six_b(cfg);
+  a.codes = codes;
+  a.scales = scales;
+  a.sdec_out = group_sdec_out;
+  a.status = d_status;
+  a.offs = offs;
+  return launch_status(fos::launch_fused_grouped(dtype, cfg->recipe, metric, prec, order, a,
+                                                 static_cast<uint32_t*>(workspace), group_amax_out,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

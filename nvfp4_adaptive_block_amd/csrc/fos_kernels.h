@@ -18,8 +18,11 @@ enum { kOutQuant = 0, kOutQdq = 1 };
 enum { kAmaxTensor = 0, kAmaxRow = 1, kAmaxBand16 = 2 };
 enum { kStatusTileNonuniform = 1, kStatusBadOffs = 2, kStatusBarrier = 4 };
 
-// Bytes of the fused kernel's workspace (its grid barrier's counters).
+// Bytes of the fused kernels' workspace (the grid barrier's counters and
+// the grouped kernel's per-group maxima), and the most groups the fused
+// grouped kernel takes.
 constexpr int kFusedWorkspaceBytes = 16384;
+constexpr int kMaxFusedGroups = 256;
 
 // Tensors per launch of the list kernel (the descriptors travel in the
 // kernel arguments, 48 B each).
@@ -75,6 +78,8 @@ hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int order
                              hipStream_t s);
 hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                         float* amax_out, hipStream_t s);
+hipError_t launch_fused_grouped(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a,
+                                uint32_t* ws, float* amax_out, hipStream_t s);
 hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, int gran,
                            const Args1x16<kMaxList>& a, hipStream_t s);
 hipError_t launch_colwise(int dt, int recipe, int metric, int prec, int order, const Args16x16& a, hipStream_t s);

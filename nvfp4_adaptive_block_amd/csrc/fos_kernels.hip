@@ -460,12 +460,13 @@ struct Walk {
   }
 };
 
-// The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED (per-
-// tensor scale only) the global amax is `fused_amax` rather than the
-// tensor's amax in memory.
+// The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED the
+// amaxes come from `fused_amax` (LDS, as float bits) rather than from
+// memory: [1] for a per-tensor scale, [G] for grouped scales.
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT, bool FUSED>
 __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
-                                          int64_t u_end, float fused_amax) {
+                                          int64_t u_end, const uint32_t* fused_amax) {
+  static_assert(!FUSED || GRAN != kGranRow, "fused amaxes: per tensor or per group");
   constexpr bool kXhat = OUT == kOutQdq;
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kNB = unit_blocks(OUT, DT) / 64;
@@ -484,7 +485,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
 
     float S_enc = 1.0f, S_dec = 1.0f;
     if (GRAN == kGranTensor) {
-      S_enc = global_encode_scale(FUSED ? fused_amax : ld_const(T.amax, 0), six_b);
+      S_enc = global_encode_scale(FUSED ? __uint_as_float(fused_amax[0]) : ld_const(T.amax, 0), six_b);
       S_dec = 1.0f / S_enc;
       tab.build(S_enc, S_dec, lane);
     }
@@ -512,7 +513,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
               g_lo = g_cur ? (int64_t)ld_const(args.offs, g_cur - 1) : 0;
               g_hi = (g_cur == args.G - 1) ? INT64_MAX : (int64_t)ld_const(args.offs, g_cur);
             }
-            A = ld_const(args.group_amax, g_cur);
+            A = FUSED ? __uint_as_float(fused_amax[g_cur]) : ld_const(args.group_amax, g_cur);
           }
           if ((int64_t)__float_as_uint(A) != tab_amax) {
             S_enc = global_encode_scale(A, six_b);
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
   const int64_t u = wave * per;
   const int64_t u_end = min(args.total_units, u + per);
   if (u >= u_end) return;
-  walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, 0.0f);
+  walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr);
 }
 
 // NaN-dropping magnitude max over packed 16-bit pairs: with m = |h| bits,
@@ -1269,8 +1270,13 @@ struct BarWs {
   __device__ uint32_t* gmax(uint32_t g) const { return w + 64 + 32 * (kBarGroups + g); }
   __device__ uint32_t* tcount() const { return w + 64 + 32 * (2 * kBarGroups); }
   __device__ uint32_t* tmax() const { return w + 64 + 32 * (2 * kBarGroups + 1); }
+  // grouped calls: their own call counter, and two banks of per-group
+  // maxima (8 bytes apart) used by alternate grouped calls
+  __device__ uint32_t* ggen() const { return w + 64 + 32 * (2 * kBarGroups + 2); }
+  __device__ uint32_t* gslot(uint32_t bank, uint32_t g) const { return w + kSlotBase + 2 * (bank * kMaxFusedGroups + g); }
+  static constexpr int kSlotBase = 64 + 32 * (2 * kBarGroups + 4);
 };
-static_assert((64 + 32 * (2 * kBarGroups + 2)) * 4 <= kFusedWorkspaceBytes, "workspace too small");
+static_assert((BarWs::kSlotBase + 4 * kMaxFusedGroups) * 4 <= kFusedWorkspaceBytes, "workspace too small");
 
 // Wait until this wave's vector memory operations (atomics included) have
 // completed; also a compiler barrier for memory operations.
@@ -1287,15 +1293,23 @@ __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::
 // invalidates the L2, which, issued by every workgroup, costs far more than
 // the barrier itself. Nothing else needs ordering: phase 2 reads only the
 // input, which the launch already sees.
-__device__ bool grid_max_barrier(const BarWs& ws, uint32_t m, uint32_t& result) {
+//
+// g0 is the generation word as read (barrier_generation) before this
+// workgroup's arrival; every workgroup of a launch reads the same value,
+// since the word changes only after all of them have arrived.
+__device__ __forceinline__ uint32_t barrier_generation(const BarWs& ws) {
+  const uint32_t g0 = __hip_atomic_load(ws.gen(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  vm_wait();
+  return g0;
+}
+
+__device__ bool grid_max_barrier(const BarWs& ws, uint32_t g0, uint32_t m, uint32_t& result) {
   constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
   constexpr int kR = __ATOMIC_RELAXED;
   const uint32_t G = gridDim.x;
   const uint32_t ng = G < (uint32_t)kBarGroups ? G : (uint32_t)kBarGroups;
   const uint32_t g = blockIdx.x % ng;
   const uint32_t gsize = G / ng + (g < G % ng ? 1u : 0u);
-  const uint32_t g0 = __hip_atomic_load(ws.gen(), kR, kA);  // before arriving
-  vm_wait();
   __hip_atomic_fetch_max(ws.gmax(g), m, kR, kA);
   vm_wait();
   if (__hip_atomic_fetch_add(ws.gcount(g), 1u, kR, kA) == gsize - 1) {
@@ -1345,7 +1359,9 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t a = 0;
-    ok = grid_max_barrier(BarWs{workspace}, max(max(part[0], part[1]), max(part[2], part[3])), a) ? 1 : 0;
+    const BarWs ws{workspace};
+    const uint32_t g0 = barrier_generation(ws);
+    ok = grid_max_barrier(ws, g0, max(max(part[0], part[1]), max(part[2], part[3])), a) ? 1 : 0;
     amax_bits = a;
     if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
   }
@@ -1359,7 +1375,107 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
 
   // phase 2
   if (u >= u_end) return;
-  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, A);
+  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, &amax_bits);
+}
+
+// Grouped (MoE) amax and quantize in one launch: the per-group amaxes the
+// grouped quantize takes as input (pytorch/ao PR, MoE commit) computed in
+// phase 1 of the same launch. Each wave takes the NaN-dropping max over the
+// part of its unit range in each group it touches (rows at or past
+// offs[G-1] are padding and are skipped); the workgroup combines its waves'
+// maxima in LDS and adds them to the group slots of the workspace with
+// atomic maxima; the grid barrier then orders every addition before any
+// read. Phase 2 is the grouped 1x16 walk with the group amaxes held in LDS.
+//
+// Slots are banked: a grouped call accumulates in bank ggen % 2 (ggen counts
+// grouped calls and is read before arriving, so every workgroup sees the
+// same value), and workgroup 0 clears all of the other bank, which the next
+// grouped call uses, and bumps ggen once the barrier has passed.
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
+__global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, uint32_t* workspace, float* amax_out) {
+  constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
+  constexpr int kR = __ATOMIC_RELAXED;
+  __shared__ float lds[4][256];
+  __shared__ uint32_t gm[kMaxFusedGroups];
+  __shared__ uint32_t gen0, bank;
+  __shared__ int ok;
+  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  const BarWs ws{workspace};
+  const int G = args.G;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
+  const int64_t u = min(args.total_units, wave * per);
+  const int64_t u_end = min(args.total_units, u + per);
+  const TensorRef& T = args.t[0];
+  const int64_t nbk = T.K >> 4, spr = (nbk + kUB - 1) / kUB;
+
+  for (int g = threadIdx.x; g < G; g += blockDim.x) gm[g] = 0u;
+  if (threadIdx.x == 0) {
+    gen0 = barrier_generation(ws);
+    bank = __hip_atomic_load(ws.ggen(), kR, kA) & 1u;
+  }
+  if (args.status) {  // the offsets contract, as the grouped quantize checks it
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t g = gid; g < G; g += (int64_t)gridDim.x * blockDim.x) {
+      const int32_t prev = g ? args.offs[g - 1] : 0;
+      const int32_t o = args.offs[g];
+      if (o < prev || (o & 15) || (g == G - 1 && (int64_t)o > T.M)) atomicOr(args.status, kStatusBadOffs);
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)  // every slot: the next grouped call may have more groups
+    for (int g = threadIdx.x; g < kMaxFusedGroups; g += blockDim.x) __hip_atomic_store(ws.gslot(bank ^ 1u, g), 0u, kR, kA);
+
+  // phase 1: the wave's units are the blocks [b0, b1) of the flattened
+  // tensor (per-row segments, in order), clipped to the rows that hold data
+  const int64_t rows_read = min(max((int64_t)ld_const(args.offs, G - 1), (int64_t)0), T.M);
+  if (u < u_end) {
+    const int64_t r0 = u / spr, r1 = (u_end - 1) / spr;
+    const int64_t b0 = r0 * nbk + (u - r0 * spr) * kUB;
+    const int64_t b1 = min(r1 * nbk + min(nbk, ((u_end - 1) - r1 * spr + 1) * kUB), rows_read * nbk);
+    if (b0 < b1) {
+      for (int g = group_of(args.offs, G, r0); g < G; g++) {
+        const int64_t g_end = (int64_t)ld_const(args.offs, g) * nbk;
+        const int64_t lo = max(b0, g ? (int64_t)ld_const(args.offs, g - 1) * nbk : (int64_t)0);
+        const int64_t hi = min(b1, g_end);
+        if (lo < hi) {
+          const uint32_t m = wave_max_u32(range_absmax<DT>(T.x, lo, hi, lane));
+          if (lane == 0 && m) atomicMax(&gm[g], m);
+        }
+        if (g_end >= b1) break;
+      }
+    }
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x)
+    if (gm[g]) __hip_atomic_fetch_max(ws.gslot(bank, g), gm[g], kR, kA);
+  vm_wait();  // this wave's additions are done before the workgroup arrives
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t unused = 0;
+    ok = grid_max_barrier(ws, gen0, 0u, unused) ? 1 : 0;
+    if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
+  }
+  __syncthreads();
+  if (!ok) return;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) gm[g] = __hip_atomic_load(ws.gslot(bank, g), kR, kA);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ws.ggen(), 1u, kR, kA);
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+      const float A = __uint_as_float(gm[g]);
+      if (amax_out) amax_out[g] = A;
+      if (args.sdec_out) args.sdec_out[g] = 1.0f / global_encode_scale(A, args.six_b);
+    }
+  }
+
+  // phase 2
+  if (u >= u_end) return;
+  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, u_end, gm);
 }
 
 // ------------------------------------------------------------ dispatch
@@ -1400,6 +1516,18 @@ static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax
   // A plain launch: a cooperative one costs about 16 us more per call on
   // this device. The grid holds only the workgroups that fit at once, so on
   // a GPU without other long-running work all of them are resident.
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
+}
+
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
+static hipError_t launch_fused_grouped_t(const Args1x16<1>& a, uint32_t* ws, float* amax_out, hipStream_t s) {
+  static_assert(GRAN == kGranGroup && OUT == kOutQuant, "fused grouped: grouped quantize only");
+  auto* fn = &k_fused_grouped<DT, RECIPE, METRIC, PREC, ORDER>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  Args1x16<1> args = a;
+  void* params[] = {&args, &ws, &amax_out};
+  // a plain launch of the resident grid, as for the per-tensor fused kernel
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 
@@ -1471,6 +1599,13 @@ hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int order
 hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                         float* amax_out, hipStream_t s) {
   FOS_DTYPES(FOS_MODES, kGranTensor, kOutQuant, CALL_F)
+}
+
+#define CALL_FG(DT, R, M, P, O, G, OUT) launch_fused_grouped_t<DT, R, M, P, O, G, OUT>(a, ws, amax_out, s)
+
+hipError_t launch_fused_grouped(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a,
+                                uint32_t* ws, float* amax_out, hipStream_t s) {
+  FOS_DTYPES(FOS_MODES, kGranGroup, kOutQuant, CALL_FG)
 }
 
 hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, int gran,

@@ -145,6 +145,39 @@ def test_grouped_moe_65536x7168(orc):
         assert int(status.item()) == 0
 
 
+def test_grouped_fused_moe_65536x7168(orc):
+    """Group amaxes and the grouped quantize in one launch on the full MoE
+    token tensor (64 groups, 4096 padding rows of garbage and NaN): all 64
+    group amaxes in full, sampled rows (every group's first and last row
+    included) against the oracle, both bounds."""
+    M, pad, K, G = 65536, 4096, 7168, 64
+    x, offs, _ = synthdata.grouped_tokens(M, pad, K, G)
+    bits = raw_bits(x)
+    starts = np.concatenate([[0], offs[:-1]]).astype(np.int64)
+    gam = np.array([orc.amax(bits[s:e], "bf16", "tensor")[0] if e > s else 0.0 for s, e in zip(starts, offs)],
+                   np.float32)
+    group_of_row = np.searchsorted(offs, np.arange(M), side="right")
+    edges = [r for s, e in zip(starts, offs) if e > s for r in (s, e - 1)]
+    rows = sample_rows(M, 96, 56, extra=edges)
+    xd = x.to("cuda")
+    od = torch.from_numpy(offs).to("cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for bound in BOUNDS:
+        kw = dict(recipe="4over6", err_metric="mse", err_prec="exact", bound=bound)
+        codes, scales, amax, gsdec = fos.fos_quantize_grouped_fused(xd, od, status=status, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), gam.view(np.uint32))
+        want = orc.quantize(bits[rows], "bf16", gam[group_of_row[rows]], scale_gran="row", **kw)
+        c = codes.cpu().numpy()
+        s = scales.cpu().numpy()
+        np.testing.assert_array_equal(s[rows], want["scales"], err_msg=f"scales bound {bound}")
+        np.testing.assert_array_equal(c[rows], want["codes"], err_msg=f"codes bound {bound}")
+        assert not c[M:].any() and not s[M:].any(), "padding rows must be zero"
+        want_sdec = np.array([orc.global_decode_scale(float(a), bound) for a in gam], np.float32)
+        np.testing.assert_array_equal(gsdec.cpu().numpy().view(np.uint32), want_sdec.view(np.uint32))
+    assert int(status.item()) == 0
+
+
 def test_fused_dense_activation_8192x4096(orc):
     """The fused amax + quantize on the full dense activation tensor, every
     mode, with one workspace across calls of two sizes."""

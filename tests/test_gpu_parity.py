@@ -261,6 +261,94 @@ def test_grouped_empty_groups_and_bad_offsets(orc):
         assert int(status.item()) & fos.STATUS_BAD_OFFS
 
 
+def _group_amaxes(orc, b, dtype, offs):
+    starts = np.concatenate([[0], offs[:-1]])
+    return np.array([orc.amax(b[s:e], dtype, "tensor")[0] if e > s else 0.0 for s, e in zip(starts, offs)],
+                    np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_grouped_fused(orc, dtype):
+    """Group amaxes and the grouped quantize in one launch equal the
+    oracle's per-group amaxes followed by its grouped quantize, for every
+    mode and both orders. Two inputs with different group scales alternate
+    on one workspace, with a per-tensor fused call in between, so a group
+    maximum left over from an earlier call would show; the padding rows hold
+    large values and NaN that must not count."""
+    M, pad, K, G = 1024, 64, 272, 16
+    xs, bs, offs_list, gams = [], [], [], []
+    for seeds in ((61, 62, 63, 64), (65, 66, 67, 68)):
+        x, offs, _ = synthdata.grouped_tokens(M, pad, K, G, seeds=seeds, dtype=dtype)
+        xs.append(x)
+        bs.append(raw_bits(x))
+        offs_list.append(offs)
+        gams.append(_group_amaxes(orc, bs[-1], dtype, offs))
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xd = [dev(x) for x in xs]
+    od = [dev(torch.from_numpy(o)) for o in offs_list]
+    modes = [(r, m, p, o) for (r, m, p) in MODES for o in (("tree", "seq") if r == "4over6" else ("tree",))]
+    for k, ((recipe, metric, prec, order), bound) in enumerate(itertools.product(modes, (448, 256))):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, err_order=order)
+        i = k % 2
+        codes, scales, gam, gsdec = fos.fos_quantize_grouped_fused(xd[i], od[i], workspace=ws, status=status, **kw)
+        torch.cuda.synchronize()
+        want = orc.quantize_grouped(bs[i], dtype, offs_list[i], gams[i], **kw)
+        np.testing.assert_array_equal(gam.cpu().numpy().view(np.uint32), gams[i].view(np.uint32), err_msg=f"{kw}")
+        np.testing.assert_array_equal(gsdec.cpu().numpy().view(np.uint32), want["group_sdec"].view(np.uint32))
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{kw}")
+        if k % 3 == 0:  # a per-tensor fused call on the same workspace
+            fos.fos_quantize_fused(xd[1 - i][:M], workspace=ws, status=status, **kw)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+
+def test_grouped_fused_edge_groups(orc):
+    """Empty groups, one group, a group holding NaN, an all-zero group, an
+    infinite element (S_enc 1 for its group), a ragged K, and offsets that
+    break the contract (status bit set)."""
+    K = 80
+    base = synthdata.normal(160, K, 5, "bf16").to(torch.float32)
+    base[100:128] = 0.0            # group 4 of the first case: all zero
+    base[40, 3] = float("nan")     # group 1: a NaN
+    base[70, 9] = float("inf")     # group 2: inf
+    base[150:] = float("nan")      # padding past offs[-1]
+    x = base.to(torch.bfloat16)
+    b = raw_bits(x)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for offs in ([0, 48, 48, 96, 128, 144], [144], [16, 16, 16, 144], [0, 0, 0]):
+        offs = np.array(offs, np.int32)
+        gam = _group_amaxes(orc, b, "bf16", offs)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        codes, scales, amax, _ = fos.fos_quantize_grouped_fused(dev(x), dev(torch.from_numpy(offs)), workspace=ws,
+                                                                status=status, recipe="4over6")
+        torch.cuda.synchronize()
+        want = orc.quantize_grouped(b, "bf16", offs, gam, recipe="4over6")
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), gam.view(np.uint32), err_msg=f"{offs}")
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{offs}")
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{offs}")
+        assert int(status.item()) == 0
+    for bad in ([0, 40, 32, 64, 64], [0, 33, 48, 64, 64], [0, 32, 48, 64, 176]):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        fos.fos_quantize_grouped_fused(dev(x), dev(torch.tensor(bad, dtype=torch.int32)), workspace=ws,
+                                       status=status, recipe="4over6")
+        torch.cuda.synchronize()
+        assert int(status.item()) & fos.STATUS_BAD_OFFS
+    # a clean call after the bad ones still matches
+    offs = np.array([0, 48, 48, 96, 128, 144], np.int32)
+    gam = _group_amaxes(orc, b, "bf16", offs)
+    codes, scales, amax, _ = fos.fos_quantize_grouped_fused(dev(x), dev(torch.from_numpy(offs)), workspace=ws,
+                                                            recipe="4over6")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), gam.view(np.uint32))
+    want = orc.quantize_grouped(b, "bf16", offs, gam, recipe="4over6")
+    np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+    with pytest.raises(fos.FosError):
+        fos.fos_quantize_grouped_fused(dev(x), dev(torch.zeros(fos.FUSED_MAX_GROUPS + 1, dtype=torch.int32)),
+                                       workspace=ws)
+
+
 # ------------------------------------------------------------------ amax
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
