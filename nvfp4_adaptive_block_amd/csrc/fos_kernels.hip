@@ -524,17 +524,42 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
           tab_row = row;
         }
       }
+      if constexpr (OUT == kOutQuant && kNB > 1) {
+        // the lane's blocks of the unit go through the fast form together,
+        // in one basic block (their serial parts interleave), and all are
+        // redone in the careful form if any holds a NaN (the careful form
+        // gives the same result on blocks without NaN)
+        float x[kNB][16], xh[kNB][16];
+        BlockOut o[kNB];
+        bool fast_ok = true;
 #pragma unroll
-      for (int j = 0; j < kNB; j++) {
-        float x[16], xh[16];
-        raw[j].unpack(x);
-        BlockOut o;
-        quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
-        if (OUT == kOutQuant) {
-          store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
-          store_scale(U.scl, off_s + j * 64, o.scale);
-        } else {
-          store16<DT>(U.out, off_x + j * 64 * kB, xh);
+        for (int j = 0; j < kNB; j++) {
+          raw[j].unpack(x[j]);
+          fast_ok &= block_1x16<RECIPE, METRIC, PREC, ORDER, false, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
+        }
+        if (!fast_ok) {
+#pragma unroll
+          for (int j = 0; j < kNB; j++)
+            block_1x16<RECIPE, METRIC, PREC, ORDER, true, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kNB; j++) {
+          store_codes(U.out, off_c + j * 64 * 8, o[j].c0, o[j].c1);
+          store_scale(U.scl, off_s + j * 64, o[j].scale);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kNB; j++) {
+          float x[16], xh[16];
+          raw[j].unpack(x);
+          BlockOut o;
+          quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
+          if (OUT == kOutQuant) {
+            store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
+            store_scale(U.scl, off_s + j * 64, o.scale);
+          } else {
+            store16<DT>(U.out, off_x + j * 64 * kB, xh);
+          }
         }
       }
     };
