@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public spec
+PEAK_VALU_LANE_TPS = 256 * 64 * 2.4e9  # VALU lane-instructions/s: 256 CUs x 64 lanes x 2.4 GHz
 MALL_BYTES = 256 << 20
 FOOTPRINT = 1 << 30            # rotate buffers up to >= 1 GiB
 METRIC = "4over6 quantize/QDQ achieved HBM GB/s and % of MI355X peak (bit-exact)"
@@ -134,7 +135,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
-              "the quantizer has no cross-GPU step here, so multi-GPU runs are not part of this build",
+              "the quantizer's step has no cross-GPU part, so it is measured on one GPU only",
               file=sys.stderr)
         sys.exit(2)
 
@@ -255,6 +256,19 @@ def main():
 
     traffic = read_counters(FUSED_KERNEL)
     rocprof_us = read_profile_value(KERNEL_TRACE, "fused_kernel_avg_us")
+    # the VALU co-bound beside the HBM one: the kernel's VALU wave
+    # instructions (SQ_INSTS_VALU of the committed counter pass) as lane
+    # instructions per second against 256 CUs x 64 lanes x 2.4 GHz
+    cf = COUNTER_FILES[FUSED_KERNEL][0]
+    wave_insts = read_profile_value(cf, "sq_insts_valu")
+    valu = None
+    if wave_insts:
+        lane_rate = wave_insts * 64 / (k_avg_ms * 1e-3)
+        valu = {"lane_insts_per_launch": int(wave_insts * 64),
+                "lane_insts_per_element": read_profile_value(cf, "valu_lane_insts_per_element"),
+                "cvt_insts_per_block": read_profile_value(cf, "valu_cvt_insts_per_block"),
+                "achieved": round(lane_rate / 1e12, 2), "peak": PEAK_VALU_LANE_TPS / 1e12,
+                "unit": "T lane-instructions/s", "frac": round(lane_rate / PEAK_VALU_LANE_TPS, 4)}
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -279,6 +293,7 @@ def main():
                      "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": round(k_avg_ms * 1e3, 2),
                      "rocprof_kernel_avg_us": rocprof_us},
+        "valu": valu,
         "barrier_ok": barrier_ok,
         "bit_exact_sample": bit_exact,
         "cpu_baseline": cpu,
