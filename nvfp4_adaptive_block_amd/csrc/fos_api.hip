@@ -311,7 +311,7 @@ int fos_quantize_grouped(const void* x, int dtype, int64_t M_alloc, int64_t K, c
   a.n = 1;
   a.G = G;
   const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
-  a.total_units = M_alloc * ((K / 16 + ub - 1) / ub);  // per-row segments
+  a.total_units = fos::grouped_units(M_alloc, a.t[0].K, ub);
   a.six_b = six_b(cfg);
   a.codes = codes;
   a.scales = scales;
@@ -411,7 +411,7 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
   a.n = 1;
   a.G = G;
   const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
-  a.total_units = M_alloc * ((K / 16 + ub - 1) / ub);  // per-row segments
+  a.total_units = fos::grouped_units(M_alloc, a.t[0].K, ub);
   a.six_b = six_b(cfg);
   a.codes = codes;
   a.scales = scales;

@@ -37,6 +37,16 @@ __host__ __device__ constexpr int unit_blocks(int out, int dt) {
   return 64 * ((out == kOutQuant && dt != kFP32) ? 2 : 1);
 }
 
+// Units of a grouped launch. A 16-row band holds K blocks and group offsets
+// are multiples of 16 rows, so when K is a multiple of the unit size every
+// group (and the padding tail) is a whole number of units: units then run
+// flat over the tensor, crossing rows but never groups, and no lane idles at
+// a row's end. Otherwise a unit is a segment of one row.
+__host__ __device__ constexpr bool grouped_flat(int64_t K, int64_t ub) { return K % ub == 0; }
+__host__ __device__ constexpr int64_t grouped_units(int64_t M, int64_t K, int64_t ub) {
+  return grouped_flat(K, ub) ? (M * (K / 16) + ub - 1) / ub : M * ((K / 16 + ub - 1) / ub);
+}
+
 // One tensor of a 1x16 launch. unit_begin: index of its first 64-block unit
 // in the launch's unit space.
 struct TensorRef {

@@ -399,11 +399,14 @@ struct Unit {
   Rsrc x, out, scl;  // input, codes (or QDQ output), scales
 };
 
-// Units of a 1x16 launch. Per-tensor scales: a unit is 64 consecutive blocks
-// of the flattened tensor. Per-row scales (and grouped): a unit is a segment
-// of up to 64 blocks of one row, so each unit has one global scale.
+// Units of a 1x16 launch. Per-tensor scales: a unit is 64·NB consecutive
+// blocks of the flattened tensor. Per-row scales: a unit is a segment of up
+// to 64·NB blocks of one row, so each unit has one global scale. Grouped
+// scales: flat units when every group is a whole number of units
+// (grouped_flat), else per-row segments.
 // Position of a unit: its index in the tensor and, for per-row units, its
-// row and segment (kept up to date incrementally: no division per unit).
+// row and segment (flat grouped units: the row of their first block and
+// that block's index in the row), kept up to date incrementally.
 struct UPos {
   int64_t v, row, seg;
 };
@@ -416,21 +419,32 @@ struct Walk {
   uint8_t* codes;
   uint8_t* scales;
   int64_t nbk, nblk, spr;
+  bool flat;  // units over the flattened tensor (per tensor, or grouped_flat)
   __device__ Walk(const TensorRef& t, uint8_t* c, uint8_t* s) : T(t), codes(c), scales(s) {
     nbk = T.K >> 4;
     nblk = T.M * nbk;
     spr = (nbk + kUnitBlocks - 1) / kUnitBlocks;
+    flat = GRAN == kGranTensor || (GRAN == kGranGroup && grouped_flat(T.K, kUnitBlocks));
   }
   __device__ UPos at(int64_t v) const {
     if (GRAN == kGranTensor) return UPos{v, 0, 0};
+    if (flat) {
+      const int64_t b0 = v * kUnitBlocks, row = b0 / nbk;
+      return UPos{v, row, b0 - row * nbk};
+    }
     const int64_t row = v / spr;
     return UPos{v, row, v - row * spr};
   }
   __device__ UPos next(UPos p) const {
     p.v += 1;
     if (GRAN != kGranTensor) {
-      p.seg += 1;
-      if (p.seg == spr) { p.seg = 0; p.row += 1; }
+      if (flat) {  // nbk >= kUnitBlocks / 16 here, so at most 16 steps
+        p.seg += kUnitBlocks;
+        while (p.seg >= nbk) { p.seg -= nbk; p.row += 1; }
+      } else {
+        p.seg += 1;
+        if (p.seg == spr) { p.seg = 0; p.row += 1; }
+      }
     }
     return p;
   }
@@ -438,7 +452,7 @@ struct Walk {
   // the tensor that hold data, later rows read as zeros)
   __device__ Unit unit(const UPos& p, bool valid, int64_t rows_read) const {
     int64_t b0, nvalid;
-    if (GRAN == kGranTensor) {
+    if (flat) {
       b0 = p.v * kUnitBlocks;
       nvalid = min((int64_t)kUnitBlocks, nblk - b0);
     } else {
@@ -460,6 +474,55 @@ struct Walk {
   }
 };
 
+// Quantize (or quantize-dequantize) the lane's blocks of one unit, held in
+// raw, and store the outputs to the unit's resources.
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int OUT>
+__device__ __forceinline__ void unit_1x16(const Raw<DT>* raw, float S_enc, float S_dec, const Table& tab,
+                                          const Unit& U, int lane) {
+  constexpr bool kXhat = OUT == kOutQdq;
+  constexpr int kB = Raw<DT>::kBytes;
+  constexpr int kNB = unit_blocks(OUT, DT) / 64;
+  const uint32_t off_x = lane * kB, off_c = lane * 8, off_s = lane;
+  if constexpr (OUT == kOutQuant && kNB > 1) {
+    // the lane's blocks of the unit go through the fast form together,
+    // in one basic block (their serial parts interleave), and all are
+    // redone in the careful form if any holds a NaN (the careful form
+    // gives the same result on blocks without NaN)
+    float x[kNB][16], xh[kNB][16];
+    BlockOut o[kNB];
+    bool fast_ok = true;
+#pragma unroll
+    for (int j = 0; j < kNB; j++) {
+      raw[j].unpack(x[j]);
+      fast_ok &= block_1x16<RECIPE, METRIC, PREC, ORDER, false, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
+    }
+    if (!fast_ok) {
+#pragma unroll
+      for (int j = 0; j < kNB; j++)
+        block_1x16<RECIPE, METRIC, PREC, ORDER, true, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kNB; j++) {
+      store_codes(U.out, off_c + j * 64 * 8, o[j].c0, o[j].c1);
+      store_scale(U.scl, off_s + j * 64, o[j].scale);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kNB; j++) {
+      float x[16], xh[16];
+      raw[j].unpack(x);
+      BlockOut o;
+      quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
+      if (OUT == kOutQuant) {
+        store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
+        store_scale(U.scl, off_s + j * 64, o.scale);
+      } else {
+        store16<DT>(U.out, off_x + j * 64 * kB, xh);
+      }
+    }
+  }
+}
+
 // The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED the
 // amaxes come from `fused_amax` (LDS, as float bits) rather than from
 // memory: [1] for a per-tensor scale, [G] for grouped scales.
@@ -467,14 +530,13 @@ template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN,
 __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
                                           int64_t u_end, const uint32_t* fused_amax) {
   static_assert(!FUSED || GRAN != kGranRow, "fused amaxes: per tensor or per group");
-  constexpr bool kXhat = OUT == kOutQdq;
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kNB = unit_blocks(OUT, DT) / 64;
   const int64_t total = args.total_units;
   int ti = 0;
   while (ti + 1 < args.n && args.t[ti + 1].unit_begin <= u) ti++;
   const float six_b = args.six_b;
-  const uint32_t off_x = lane * kB, off_c = lane * 8, off_s = lane;
+  const uint32_t off_x = lane * kB;
 
   for (;;) {
     const TensorRef T = args.t[ti];
@@ -524,44 +586,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
           tab_row = row;
         }
       }
-      if constexpr (OUT == kOutQuant && kNB > 1) {
-        // the lane's blocks of the unit go through the fast form together,
-        // in one basic block (their serial parts interleave), and all are
-        // redone in the careful form if any holds a NaN (the careful form
-        // gives the same result on blocks without NaN)
-        float x[kNB][16], xh[kNB][16];
-        BlockOut o[kNB];
-        bool fast_ok = true;
-#pragma unroll
-        for (int j = 0; j < kNB; j++) {
-          raw[j].unpack(x[j]);
-          fast_ok &= block_1x16<RECIPE, METRIC, PREC, ORDER, false, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
-        }
-        if (!fast_ok) {
-#pragma unroll
-          for (int j = 0; j < kNB; j++)
-            block_1x16<RECIPE, METRIC, PREC, ORDER, true, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < kNB; j++) {
-          store_codes(U.out, off_c + j * 64 * 8, o[j].c0, o[j].c1);
-          store_scale(U.scl, off_s + j * 64, o[j].scale);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kNB; j++) {
-          float x[16], xh[16];
-          raw[j].unpack(x);
-          BlockOut o;
-          quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
-          if (OUT == kOutQuant) {
-            store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
-            store_scale(U.scl, off_s + j * 64, o.scale);
-          } else {
-            store16<DT>(U.out, off_x + j * 64 * kB, xh);
-          }
-        }
-      }
+      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, OUT>(raw, S_enc, S_dec, tab, U, lane);
     };
 
     auto load_unit = [&](Raw<DT>* r, const Unit& U) {
@@ -1403,6 +1428,161 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
   walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, &amax_bits);
 }
 
+// ------------------------------------------------------------ on-chip fused amax + quantize
+
+// The fused amax and quantize for a tensor that fits on chip: when no wave
+// has more than kOnchipUnits units, each wave reads its units once, the
+// first kOnchipLds of them straight into a wave-private LDS stage (direct
+// buffer loads: lane l's 16-byte piece k of a unit lands at
+// stage + 1024 k + 16 l) and the rest into registers, takes their
+// NaN-dropping max, passes the grid barrier of k_fused, and quantizes from
+// the stage and the registers. Phase 2 reads nothing from memory, so the
+// launch moves each input byte once (k_fused reads it twice).
+constexpr int kOnchipLds = 2;  // units per wave staged in LDS
+constexpr int kOnchipReg = 2;  // units per wave held in registers
+constexpr int kOnchipUnits = kOnchipLds + kOnchipReg;
+
+// Piece k (16 bytes) of a lane's part of a quantize unit: its byte offset in
+// the unit, and the register it is held in (16-bit types: two blocks of two
+// pieces; fp32: one block of four).
+template <int DT>
+__device__ __forceinline__ uint32_t piece_offset(int lane, int k) {
+  if (DT == kFP32) return lane * 64 + k * 16;
+  return (k >> 1) * 64 * 32 + lane * 32 + (k & 1) * 16;
+}
+// Direct load to LDS: each lane reads 16 bytes at voffset of r and the
+// hardware writes lane l's bytes to dst + 16 l (64 lanes: 1 KiB).
+__device__ __forceinline__ void load_lds16(Rsrc r, v4i* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ v4i& piece(Raw<DT>* r, int k) {
+  if constexpr (DT == kFP32) return r[0].v[k];
+  else return (k & 1) ? r[k >> 1].b : r[k >> 1].a;
+}
+
+// Running NaN-dropping max |x| of raw pieces: magnitude bits for fp32,
+// packed 16-bit keys for the 16-bit types.
+template <int DT>
+struct PieceMax {
+  uint32_t m = 0;
+  s16x2 k = pair_key<DT>(0u);
+  __device__ void add(const v4i p) {
+    if constexpr (DT == kFP32) {
+      m = max(max(m, mag_bits(__int_as_float(p.x))), max(mag_bits(__int_as_float(p.y)),
+              max(mag_bits(__int_as_float(p.z)), mag_bits(__int_as_float(p.w)))));
+    } else {
+      k = __builtin_elementwise_max(k, pair_key<DT>((uint32_t)p.x));
+      k = __builtin_elementwise_max(k, pair_key<DT>((uint32_t)p.y));
+      k = __builtin_elementwise_max(k, pair_key<DT>((uint32_t)p.z));
+      k = __builtin_elementwise_max(k, pair_key<DT>((uint32_t)p.w));
+    }
+  }
+  __device__ uint32_t bits() const {
+    if constexpr (DT == kFP32) return m;
+    else return pair_key_to_f32_bits<DT>(k);
+  }
+};
+
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
+__global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, uint32_t* workspace, float* amax_out) {
+  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  constexpr int kNB = kUB / 64;
+  constexpr int kB = Raw<DT>::kBytes;
+  constexpr int kPieces = kNB * kB / 16;
+  static_assert(sizeof(Raw<DT>) * kNB == 16 * kPieces, "a lane's unit is kPieces 16-byte pieces");
+  __shared__ float lds[4][256];
+  __shared__ v4i stage[4][kOnchipLds][kPieces][64];
+  __shared__ uint32_t part[4];
+  __shared__ uint32_t amax_bits;
+  __shared__ int ok;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (args.total_units + nwaves - 1) / nwaves;  // <= kOnchipUnits (the launch checks)
+  const int64_t u = min(args.total_units, wave * per);
+  const int64_t u_end = min(args.total_units, u + per);
+  const TensorRef& T = args.t[0];
+  const int64_t nblk = T.M * (T.K >> 4);
+  const Walk<DT, kGranTensor, kOutQuant> W(T, args.codes, args.scales);
+
+  // phase 1: read every unit once; units past the wave's range have empty
+  // resources (their loads read zeros and are never used)
+  Raw<DT> R[kOnchipReg][kNB];
+#pragma unroll
+  for (int t = 0; t < kOnchipLds; t++) {
+    const Unit U = W.unit(W.at(u + t), u + t < u_end, T.M);
+#pragma unroll
+    for (int k = 0; k < kPieces; k++) load_lds16(U.x, &stage[wv][t][k][0], piece_offset<DT>(lane, k));
+  }
+#pragma unroll
+  for (int r = 0; r < kOnchipReg; r++) {
+    const Unit U = W.unit(W.at(u + kOnchipLds + r), u + kOnchipLds + r < u_end, T.M);
+#pragma unroll
+    for (int j = 0; j < kNB; j++) R[r][j].load(U.x, lane * kB + j * 64 * kB);
+  }
+  vm_wait();  // the loads, the LDS-bound ones included, have landed
+  PieceMax<DT> pm;
+#pragma unroll
+  for (int t = 0; t < kOnchipLds; t++) {
+    // only blocks of the tensor count: a stage lane past its end holds
+    // whatever an earlier launch left there
+    const int64_t nvalid = (u + t < u_end) ? min((int64_t)kUB, nblk - (u + t) * kUB) : 0;
+#pragma unroll
+    for (int k = 0; k < kPieces; k++) {
+      const int64_t blk = (DT == kFP32) ? lane : (k >> 1) * 64 + lane;
+      if (blk < nvalid) pm.add(stage[wv][t][k][lane]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kOnchipReg; r++)
+#pragma unroll
+    for (int k = 0; k < kPieces; k++) pm.add(piece<DT>(R[r], k));
+  const uint32_t m = wave_max_u32(pm.bits());
+  if (lane == 0) part[wv] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    const BarWs ws{workspace};
+    const uint32_t g0 = barrier_generation(ws);
+    ok = grid_max_barrier(ws, g0, max(max(part[0], part[1]), max(part[2], part[3])), a) ? 1 : 0;
+    amax_bits = a;
+    if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
+  }
+  __syncthreads();
+  if (!ok) return;
+  const float A = __uint_as_float(amax_bits);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (amax_out) amax_out[0] = A;
+    if (args.sdec_out) args.sdec_out[0] = 1.0f / global_encode_scale(A, args.six_b);
+  }
+
+  // phase 2: quantize the register units, then the staged ones
+  if (u >= u_end) return;
+  const float S_enc = global_encode_scale(A, args.six_b);
+  const float S_dec = 1.0f / S_enc;
+  tab.build(S_enc, S_dec, lane);
+#pragma unroll
+  for (int r = 0; r < kOnchipReg; r++) {
+    const int64_t v = u + kOnchipLds + r;
+    if (v < u_end)
+      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, kOutQuant>(R[r], S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
+  }
+#pragma unroll
+  for (int t = 0; t < kOnchipLds; t++) {
+    const int64_t v = u + t;
+    if (v < u_end) {
+      Raw<DT> q[kNB];
+#pragma unroll
+      for (int k = 0; k < kPieces; k++) piece<DT>(q, k) = stage[wv][t][k][lane];
+      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, kOutQuant>(q, S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
+    }
+  }
+}
+
 // Grouped (MoE) amax and quantize in one launch: the per-group amaxes the
 // grouped quantize takes as input (pytorch/ao PR, MoE commit) computed in
 // phase 1 of the same launch. Each wave takes the NaN-dropping max over the
@@ -1437,6 +1617,7 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
   const int64_t u_end = min(args.total_units, u + per);
   const TensorRef& T = args.t[0];
   const int64_t nbk = T.K >> 4, spr = (nbk + kUB - 1) / kUB;
+  const bool flat = grouped_flat(T.K, kUB);
 
   for (int g = threadIdx.x; g < G; g += blockDim.x) gm[g] = 0u;
   if (threadIdx.x == 0) {
@@ -1456,12 +1637,21 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
     for (int g = threadIdx.x; g < kMaxFusedGroups; g += blockDim.x) __hip_atomic_store(ws.gslot(bank ^ 1u, g), 0u, kR, kA);
 
   // phase 1: the wave's units are the blocks [b0, b1) of the flattened
-  // tensor (per-row segments, in order), clipped to the rows that hold data
+  // tensor (flat units, or per-row segments in order), clipped to the rows
+  // that hold data
   const int64_t rows_read = min(max((int64_t)ld_const(args.offs, G - 1), (int64_t)0), T.M);
   if (u < u_end) {
-    const int64_t r0 = u / spr, r1 = (u_end - 1) / spr;
-    const int64_t b0 = r0 * nbk + (u - r0 * spr) * kUB;
-    const int64_t b1 = min(r1 * nbk + min(nbk, ((u_end - 1) - r1 * spr + 1) * kUB), rows_read * nbk);
+    int64_t r0, b0, b1;
+    if (flat) {
+      b0 = u * kUB;
+      b1 = min(min(u_end * kUB, T.M * nbk), rows_read * nbk);
+      r0 = b0 / nbk;
+    } else {
+      r0 = u / spr;
+      const int64_t r1 = (u_end - 1) / spr;
+      b0 = r0 * nbk + (u - r0 * spr) * kUB;
+      b1 = min(r1 * nbk + min(nbk, ((u_end - 1) - r1 * spr + 1) * kUB), rows_read * nbk);
+    }
     if (b0 < b1) {
       for (int g = group_of(args.offs, G, r0); g < G; g++) {
         const int64_t g_end = (int64_t)ld_const(args.offs, g) * nbk;
@@ -1534,10 +1724,18 @@ template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT
 static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax_out, hipStream_t s) {
   static_assert(GRAN == kGranTensor && OUT == kOutQuant, "fused: per-tensor quantize only");
   auto* fn = &k_fused<DT, RECIPE, METRIC, PREC, ORDER>;
+  auto* fn_chip = &k_fused_onchip<DT, RECIPE, METRIC, PREC, ORDER>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
-  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  static const int64_t resident_chip = resident_grid(reinterpret_cast<const void*>(fn_chip));
+  // the on-chip form when its resident grid leaves each wave at most
+  // kOnchipUnits units (the tensor then fits in the waves' registers and
+  // LDS stages), else the two-read form
+  const int64_t grid_chip = max((int64_t)1, min(resident_chip, (a.total_units + 3) / 4));
+  const bool chip = a.total_units <= grid_chip * 4 * kOnchipUnits;
+  const int64_t grid = chip ? grid_chip : max((int64_t)1, min(resident, (a.total_units + 3) / 4));
   Args1x16<1> args = a;
   void* params[] = {&args, &ws, &amax_out};
+  if (chip) return hipLaunchKernel(reinterpret_cast<const void*>(fn_chip), dim3((unsigned)grid), dim3(256), params, 0, s);
   // A plain launch: a cooperative one costs about 16 us more per call on
   // this device. The grid holds only the workgroups that fit at once, so on
   // a GPU without other long-running work all of them are resident.

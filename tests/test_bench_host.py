@@ -37,7 +37,9 @@ def test_kernel_descriptions():
         "1x16 quantize bf16 4over6 mse exact tensor"
     assert d("void fos::k_1x16<48, 1, 1, 0, 1, 1, 0, 1>(fos::Args1x16<48>)") == \
         "1x16 qdq list<48> fp16 4over6 mae fp16err seq tensor"
-    assert d(bench.FUSED_KERNEL) == "fused amax + 1x16 quantize bf16 4over6 mse exact tensor"
+    assert d(bench.FUSED_KERNEL) == "fused amax + 1x16 quantize (one read) bf16 4over6 mse exact tensor"
+    assert d("void fos::k_fused<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)") == \
+        "fused amax + 1x16 quantize (two reads) bf16 4over6 mse exact tensor"
     assert d("void fos::k_16x16<2, 1, 1, 0, 1, 0>(fos::Args16x16)").startswith("16x16 quantize fp32 4over6")
     assert "grouped" in d("void fos::k_fused_grouped<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)")
     assert d("void fos::k_colwise<0, 1, 1, 0, 0>(fos::Args16x16)").startswith("columnwise")
@@ -46,9 +48,10 @@ def test_kernel_descriptions():
 
 
 def test_step_bytes_of_the_dense_activation_step():
-    # per 1x16 block: amax read 32 B + quantize read 32 B + codes 8 B + scale 1 B
+    # per 1x16 block: one read of 32 B (the amax and the quantize share it,
+    # the tensor staying on chip in between) + codes 8 B + scale 1 B
     M, K = 8192, 4096
     blocks = M * K // 16
-    assert blocks * 73 == 153092096
-    assert bench.COUNTER_FILES[bench.FUSED_KERNEL][2] == 153092096
+    assert blocks * 41 == 85983232
+    assert bench.COUNTER_FILES[bench.FUSED_KERNEL][2] == 85983232
     assert bench.COUNTER_FILES[bench.QUANT_KERNEL][2] == blocks * 41

@@ -205,6 +205,28 @@ def test_fused_dense_activation_8192x4096(orc):
     assert not ws[256:].any()
 
 
+def test_fused_beyond_one_read_16384x4096(orc):
+    """A tensor too large for the one-read fused form (twice the dense
+    activation tensor) takes the two-read form; sampled rows against the
+    oracle, for the standard recipe and four-over-six."""
+    M, K = 16384, 4096
+    x = synthdata.activation_family("outlier", M, K, 25, "bf16")
+    bits = raw_bits(x)
+    xd = x.to("cuda")
+    a = orc.amax(bits, "bf16", "tensor")
+    rows = sample_rows(M, 48, 25)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for recipe, metric, prec in (("nvfp4", "mse", "exact"), ("4over6", "mse", "exact"), ("4over6", "mae", "fp16")):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec)
+        codes, scales, amax, _ = fos.fos_quantize_fused(xd, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        want = orc.quantize(bits[rows], "bf16", a, **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"{kw}")
+    assert not ws[256:].any()
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("gran", ["tensor", "row"])
 def test_dequantize_8192x4096(orc, out_dtype, gran):

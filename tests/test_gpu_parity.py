@@ -242,6 +242,37 @@ def test_grouped_small(orc, bound):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("K", [128, 384])
+def test_grouped_flat_units(orc, dtype, K):
+    """K a multiple of the unit size: every 16-row band is a whole number of
+    units, so the grouped walk runs flat units that cross rows (K = 384: a
+    unit spans 5.3 rows of bf16 blocks) but never groups. Both grouped entry
+    points equal the oracle's grouped quantize, empty groups and the padding
+    tail included."""
+    M, pad, G = 512, 48, 12
+    x, offs, _ = synthdata.grouped_tokens(M, pad, K, G, seeds=(71, 72, 73, 74), dtype=dtype)
+    b = raw_bits(x)
+    gam = _group_amaxes(orc, b, dtype, offs)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for metric, prec in (("mse", "exact"), ("mae", "fp16")):
+        kw = dict(recipe="4over6", err_metric=metric, err_prec=prec)
+        want = orc.quantize_grouped(b, dtype, offs, gam, **kw)
+        codes, scales, _ = fos.fos_quantize_grouped(dev(x), dev(torch.from_numpy(offs)), dev(torch.from_numpy(gam)),
+                                                    status=status, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{kw}")
+        codes, scales, am, _ = fos.fos_quantize_grouped_fused(dev(x), dev(torch.from_numpy(offs)), workspace=ws,
+                                                              status=status, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(am.cpu().numpy().view(np.uint32), gam.view(np.uint32), err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{kw}")
+    assert int(status.item()) == 0
+
+
 def test_grouped_empty_groups_and_bad_offsets(orc):
     K = 64
     x = synthdata.normal(96, K, 3, "bf16")
@@ -440,6 +471,28 @@ def test_fused_amax_quantize(orc, dtype):
             np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{M}x{K} {kw}")
             np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{M}x{K} {kw}")
             assert not ws[256:].any(), "the workspace's counters must be zero after a call"
+    assert int(status.item()) == 0
+
+
+def test_fused_stage_lanes_past_the_end(orc):
+    """Small tensors take the one-read fused form, whose waves stage units in
+    LDS; a stage lane past the tensor's end holds what an earlier launch
+    left there and must not count in the amax. A launch over large values
+    fills the stages first, then ragged tensors of small values follow."""
+    big = (synthdata.normal(512, 4096, 81, "bf16").to(torch.float32) * 1e30).to(torch.bfloat16)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for dtype, (M, K) in (("bf16", (67, 1552)), ("fp32", (5, 208)), ("fp16", (33, 4112))):
+        fos.fos_quantize_fused(dev(big), workspace=ws, status=status, recipe="4over6")
+        x = synthdata.normal(M, K, 82, dtype)
+        b = raw_bits(x)
+        a = orc.amax(b, dtype, "tensor")
+        codes, scales, amax, _ = fos.fos_quantize_fused(dev(x), workspace=ws, status=status, recipe="4over6")
+        torch.cuda.synchronize()
+        want = orc.quantize(b, dtype, a, recipe="4over6")
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32), err_msg=dtype)
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=dtype)
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=dtype)
     assert int(status.item()) == 0
 
 
