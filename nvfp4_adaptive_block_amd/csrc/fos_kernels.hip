@@ -98,6 +98,11 @@ template <> struct Raw<kFP32> {
   }
 };
 
+// Cache policy of the output stores: non-temporal. No kernel reads its
+// outputs back, and streaming them past the caches measured 4-11 % faster
+// (quantize, fused amax + quantize, fused QDQ) than default stores.
+constexpr int kStoreNT = 2;
+
 // Store 16 decoded values as the tensor's element type.
 template <int DT> __device__ __forceinline__ void store16(Rsrc r, uint32_t off, const float* y);
 
@@ -106,23 +111,23 @@ template <> __device__ __forceinline__ void store16<kBF16>(Rsrc r, uint32_t off,
                  (int)pack_bf16(y[6], y[7])};
   const v4i b = {(int)pack_bf16(y[8], y[9]), (int)pack_bf16(y[10], y[11]), (int)pack_bf16(y[12], y[13]),
                  (int)pack_bf16(y[14], y[15])};
-  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, kStoreNT);
+  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, kStoreNT);
 }
 template <> __device__ __forceinline__ void store16<kFP16>(Rsrc r, uint32_t off, const float* y) {
   const v4i a = {(int)pack_f16(y[0], y[1]), (int)pack_f16(y[2], y[3]), (int)pack_f16(y[4], y[5]),
                  (int)pack_f16(y[6], y[7])};
   const v4i b = {(int)pack_f16(y[8], y[9]), (int)pack_f16(y[10], y[11]), (int)pack_f16(y[12], y[13]),
                  (int)pack_f16(y[14], y[15])};
-  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, kStoreNT);
+  __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, kStoreNT);
 }
 template <> __device__ __forceinline__ void store16<kFP32>(Rsrc r, uint32_t off, const float* y) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const v4i a = {__float_as_int(y[4 * i]), __float_as_int(y[4 * i + 1]), __float_as_int(y[4 * i + 2]),
                    __float_as_int(y[4 * i + 3])};
-    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * i, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * i, 0, kStoreNT);
   }
 }
 
@@ -131,29 +136,29 @@ template <int DT> __device__ __forceinline__ void store8(Rsrc r, uint32_t off, c
 template <> __device__ __forceinline__ void store8<kBF16>(Rsrc r, uint32_t off, const float* y) {
   const v4i a = {(int)pack_bf16(y[0], y[1]), (int)pack_bf16(y[2], y[3]), (int)pack_bf16(y[4], y[5]),
                  (int)pack_bf16(y[6], y[7])};
-  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, kStoreNT);
 }
 template <> __device__ __forceinline__ void store8<kFP16>(Rsrc r, uint32_t off, const float* y) {
   const v4i a = {(int)pack_f16(y[0], y[1]), (int)pack_f16(y[2], y[3]), (int)pack_f16(y[4], y[5]),
                  (int)pack_f16(y[6], y[7])};
-  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, kStoreNT);
 }
 template <> __device__ __forceinline__ void store8<kFP32>(Rsrc r, uint32_t off, const float* y) {
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const v4i a = {__float_as_int(y[4 * i]), __float_as_int(y[4 * i + 1]), __float_as_int(y[4 * i + 2]),
                    __float_as_int(y[4 * i + 3])};
-    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * i, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * i, 0, kStoreNT);
   }
 }
 
 __device__ __forceinline__ void store_codes(Rsrc r, uint32_t off, uint32_t c0, uint32_t c1) {
   const v2i v = {(int)c0, (int)c1};
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStoreNT);
 }
 
 __device__ __forceinline__ void store_scale(Rsrc r, uint32_t off, uint32_t s) {
-  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)s, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)s, r, off, 0, kStoreNT);
 }
 
 // Stores that touch nothing (zero-range resource), fenced against
