@@ -224,7 +224,7 @@ int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, cons
  * FOS_PER_TENSOR.
  *   amax_out:  nullable device float[1], receives the NaN-dropping max |x|.
  *   sdec_out:  nullable device float[1], receives S_dec.
- *   workspace: device memory of FOS_FUSED_WORKSPACE_BYTES, 4-byte aligned,
+ *   workspace: device memory of FOS_FUSED_WORKSPACE_BYTES, 8-byte aligned,
  *              all zero before its first use (e.g. cleared once at
  *              allocation). Every completed call leaves its counters zero
  *              again (only the first 256 bytes, a call counter and the last

@@ -365,7 +365,7 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   if (M * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
   if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
   if (!aligned(x, 16) || !aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "x or codes misaligned");
-  if (!aligned(workspace, 4) || !aligned(amax_out, 4) || !aligned(sdec_out, 4) || !aligned(d_status, 4))
+  if (!aligned(workspace, 8) || !aligned(amax_out, 4) || !aligned(sdec_out, 4) || !aligned(d_status, 4))
     return fail(FOS_ERR_ALIGN, "workspace/amax/sdec/status misaligned");
   if ((rc = check_device())) return rc;
   int metric, prec, order;
@@ -400,7 +400,7 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
   if (M_alloc * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
   if (!aligned(x, 16) || !aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "x or codes misaligned");
   if (!aligned(offs, 4) || !aligned(group_amax_out, 4) || !aligned(group_sdec_out, 4) || !aligned(d_status, 4) ||
-      !aligned(workspace, 4))
+      !aligned(workspace, 8))
     return fail(FOS_ERR_ALIGN, "offs/amax/sdec/status/workspace misaligned");
   if ((rc = check_device())) return rc;
   int metric, prec, order;

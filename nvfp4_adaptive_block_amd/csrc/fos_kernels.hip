@@ -100,7 +100,10 @@ template <> struct Raw<kFP32> {
 
 // Cache policy of the output stores: non-temporal. No kernel reads its
 // outputs back, and streaming them past the caches measured 4-11 % faster
-// (quantize, fused amax + quantize, fused QDQ) than default stores.
+// (quantize, fused amax + quantize, fused QDQ) than default stores. The
+// columnwise kernel's whole-line stores keep the default policy: its scale
+// lines are assembled from eight tiles in one L2, and non-temporal stores
+// there measured slower.
 constexpr int kStoreNT = 2;
 
 // Store 16 decoded values as the tensor's element type.
@@ -1316,11 +1319,12 @@ constexpr int kBarGroups = 32;       // first-level arrival groups
 constexpr int kSpinLimit = 1 << 20;  // polls before giving up (each at least 128 cycles of sleep)
 
 // Word offsets in the workspace; every counter and maximum sits on a
-// 128-byte line of its own.
+// 128-byte line of its own. The published word (8-byte aligned) holds the
+// barrier's generation in its low half and the launch's combined maximum in
+// its high half, so one 64-bit store publishes both and one load reads both.
 struct BarWs {
   uint32_t* w;
-  __device__ uint32_t* gen() const { return w; }
-  __device__ uint32_t* result() const { return w + 32; }
+  __device__ uint64_t* pub() const { return reinterpret_cast<uint64_t*>(w); }
   __device__ uint32_t* gcount(uint32_t g) const { return w + 64 + 32 * g; }
   __device__ uint32_t* gmax(uint32_t g) const { return w + 64 + 32 * (kBarGroups + g); }
   __device__ uint32_t* tcount() const { return w + 64 + 32 * (2 * kBarGroups); }
@@ -1353,9 +1357,9 @@ __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::
 // workgroup's arrival; every workgroup of a launch reads the same value,
 // since the word changes only after all of them have arrived.
 __device__ __forceinline__ uint32_t barrier_generation(const BarWs& ws) {
-  const uint32_t g0 = __hip_atomic_load(ws.gen(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t p = __hip_atomic_load(ws.pub(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   vm_wait();
-  return g0;
+  return (uint32_t)p;
 }
 
 __device__ bool grid_max_barrier(const BarWs& ws, uint32_t g0, uint32_t m, uint32_t& result) {
@@ -1376,16 +1380,16 @@ __device__ bool grid_max_barrier(const BarWs& ws, uint32_t g0, uint32_t m, uint3
     if (__hip_atomic_fetch_add(ws.tcount(), 1u, kR, kA) == ng - 1) {
       const uint32_t a = __hip_atomic_exchange(ws.tmax(), 0u, kR, kA);
       __hip_atomic_store(ws.tcount(), 0u, kR, kA);
-      __hip_atomic_store(ws.result(), a, kR, kA);
-      vm_wait();
-      __hip_atomic_fetch_add(ws.gen(), 1u, kR, kA);
+      __hip_atomic_store(ws.pub(), ((uint64_t)a << 32) | (uint64_t)(g0 + 1u), kR, kA);
     }
   }
-  for (int it = 0; __hip_atomic_load(ws.gen(), kR, kA) == g0; it++) {
+  uint64_t p = __hip_atomic_load(ws.pub(), kR, kA);
+  for (int it = 0; (uint32_t)p == g0; it++) {
     if (it >= kSpinLimit) return false;
     __builtin_amdgcn_s_sleep(2);
+    p = __hip_atomic_load(ws.pub(), kR, kA);
   }
-  result = __hip_atomic_load(ws.result(), kR, kA);
+  result = (uint32_t)(p >> 32);
   return true;
 }
 
