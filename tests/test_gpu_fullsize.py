@@ -205,6 +205,29 @@ def test_fused_dense_activation_8192x4096(orc):
     assert not ws[256:].any()
 
 
+@pytest.mark.parametrize("dtype,M,K", [("fp32", 4096, 4096), ("fp32", 4096, 4112), ("fp16", 8192, 4096),
+                                       ("fp16", 8192, 4112)])
+def test_fused_at_the_one_read_capacity(orc, dtype, M, K):
+    """The fused amax + quantize right at the capacity of its one-read form
+    (fp32 4096x4096 and fp16 8192x4096 fill it exactly) and just past it
+    (K = 4112: the two-read form); sampled rows against the oracle."""
+    x = synthdata.activation_family("outlier", M, K, 27, dtype)
+    bits = raw_bits(x)
+    xd = x.to("cuda")
+    a = orc.amax(bits, dtype, "tensor")
+    rows = sample_rows(M, 32, 27)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for recipe, metric, prec in (("4over6", "mse", "exact"), ("4over6", "mae", "fp16")):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec)
+        codes, scales, amax, _ = fos.fos_quantize_fused(xd, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        want = orc.quantize(bits[rows], dtype, a, **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"{kw}")
+    assert not ws[256:].any()
+
+
 def test_fused_beyond_one_read_16384x4096(orc):
     """A tensor too large for the one-read fused form (twice the dense
     activation tensor) takes the two-read form; sampled rows against the
