@@ -494,6 +494,18 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
                                                             "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
     log(f"[bench] quantize bf16 8192x4096, precomputed amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
 
+    # the same tensor with per-row global scales (one amax per row)
+    row_amax = [fos.fos_amax(xs[i], "row") for i in range(len(xs))]
+    rknobs = dict(knobs, scale_gran="row")
+    rsdec = torch.empty(xs[0].shape[0], dtype=torch.float32, device="cuda")
+    _, ms = time_loop(lambda i: fos.fos_quantize(xs[i], row_amax[i], codes=codes[i], scales=scales[i], sdec=rsdec,
+                                                 **rknobs), len(xs), 200, 10)
+    avg = float(np.median(ms))
+    out["quantize_1x16_bf16_8192x4096_per_row_amax"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
+                                                        "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
+    log(f"[bench] quantize bf16 8192x4096, per-row amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
+    del row_amax
+
     def two_launches(i):
         fos.fos_amax(xs[i], "tensor", out=amax[i])
         fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)
