@@ -506,6 +506,23 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
     log(f"[bench] quantize bf16 8192x4096, per-row amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
     del row_amax
 
+    # fused fake quantization of the same tensor with its amax computed on
+    # the device: one launch that reads x once, against fos_amax + fos_qdq
+    ys2 = [torch.empty_like(x) for x in xs]
+    qkw = dict(recipe="4over6", err_metric="mse", err_prec="fp16", bound=448)
+    qws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    qb2 = n * 2 + n * 2
+    for key, fn in (("qdq_fused_amax_bf16_8192x4096_4over6_mse_fp16_448",
+                     lambda i: fos.fos_qdq_fused(xs[i], out=ys2[i], amax=amax[i], workspace=qws, **qkw)),
+                    ("amax_then_qdq_bf16_8192x4096_4over6_mse_fp16_448",
+                     lambda i: (fos.fos_amax(xs[i], "tensor", out=amax[i]),
+                                fos.fos_qdq(xs[i], amax[i], out=ys2[i], **qkw)))):
+        _, ms = time_loop(fn, len(xs), 200, 10)
+        avg = float(np.median(ms))
+        out[key] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb2, avg), "frac": round(gbs(qb2, avg) / PEAK_HBM_GBS, 4)}
+        log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(qb2, avg):.0f} GB/s (x read once, y written)")
+    del ys2
+
     def two_launches(i):
         fos.fos_amax(xs[i], "tensor", out=amax[i])
         fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)

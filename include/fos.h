@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FOS_ABI_VERSION 3
+#define FOS_ABI_VERSION 4
 
 /* element types */
 #define FOS_BF16 0
@@ -112,8 +112,8 @@ extern "C" {
 #define FOS_STATUS_BARRIER_TIMEOUT 4 /* fused calls: the grid barrier did not complete (workspace not zero) */
 
 /* Bytes of the device workspace the fused calls (fos_quantize_fused,
- * fos_quantize_grouped_fused) need; the most groups the fused grouped call
- * takes (added in ABI version 3). */
+ * fos_quantize_grouped_fused, fos_qdq_fused) need; the most groups the fused
+ * grouped call takes (added in ABI version 3). */
 #define FOS_FUSED_WORKSPACE_BYTES 16384
 #define FOS_FUSED_MAX_GROUPS 256
 
@@ -243,6 +243,21 @@ int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, cons
 int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
                        uint8_t* scales, float* amax_out, float* sdec_out, void* workspace, int32_t* d_status,
                        void* stream);
+
+/* Per-tensor amax and fused fake quantization in one launch (added in ABI
+ * version 4): the amax pre-pass of the Megatron-LM PR's fake-quantization
+ * loop ("What does this PR do?": a separate FP32 reduction per weight before
+ * the fused data path) folded into fos_qdq. The result equals
+ * fos_amax(..., FOS_AMAX_TENSOR) followed by fos_qdq with that amax, bit for
+ * bit. cfg must be 1x16 with FOS_PER_TENSOR; x and y are bf16, fp16 or fp32.
+ * A tensor that fits on chip (up to 32 M elements of a 16-bit type or 16 M
+ * fp32 on a 256-CU device) takes one launch that reads x from memory once;
+ * a larger one takes the amax launch and the QDQ launch.
+ *   y:         device [M, K] of x's type, 16-byte aligned.
+ *   amax_out:  device float[1] (not NULL), receives the NaN-dropping max |x|.
+ *   workspace, d_status: as for fos_quantize_fused. */
+int fos_qdq_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, void* y, float* amax_out,
+                  void* workspace, int32_t* d_status, void* stream);
 
 /* Grouped (MoE) amax and quantize in one launch: the group amaxes that
  * fos_quantize_grouped takes as input (pytorch/ao PR, MoE commit; the

@@ -65,6 +65,7 @@ _SIGS = {
     "nvfp4_dequantize": (_I, [_P, _P, _I64, _I64, _P, _I, _I, _P, _P]),
     "fos_quantize_grouped": (_I, [_P, _I, _I64, _I64, _P, _I, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_quantize_fused": (_I, [_P, _I, _I64, _I64, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P, _P]),
+    "fos_qdq_fused": (_I, [_P, _I, _I64, _I64, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_quantize_columnwise": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P]),
     "fos_quantize_grouped_fused": (_I, [_P, _I, _I64, _I64, _P, _I, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P,
                                         _P]),
@@ -187,6 +188,24 @@ def fos_quantize_fused(x: torch.Tensor, *, codes=None, scales=None, amax=None, s
                                                  _ptr(scales), _ptr(amax), _ptr(sdec), _ptr(workspace),
                                                  _ptr(status), _stream(dev)))
     return codes, scales, amax, sdec
+
+
+def fos_qdq_fused(x: torch.Tensor, *, out=None, amax=None, status=None, workspace=None, **knobs):
+    """Per-tensor amax and fused quantize-dequantize in one launch (two when
+    the tensor does not fit on chip). Returns (y, amax float32[1])."""
+    _need(x, "x")
+    M, K = x.shape
+    cfg = config(**knobs)
+    dev = x.device
+    y = torch.empty_like(x) if out is None else out
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = fused_workspace(dev)
+    with torch.cuda.device(dev):
+        _check(load_library().fos_qdq_fused(_ptr(x), DTYPES[x.dtype], M, K, ctypes.byref(cfg), _ptr(y), _ptr(amax),
+                                            _ptr(workspace), _ptr(status), _stream(dev)))
+    return y, amax
 
 
 def fos_quantize_columnwise(x: torch.Tensor, amax: torch.Tensor, *, codes=None, scales=None, sdec=None, **knobs):

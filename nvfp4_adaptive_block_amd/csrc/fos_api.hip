@@ -385,6 +385,42 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
                                          amax_out, static_cast<hipStream_t>(stream)));
 }
 
+int fos_qdq_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, void* y, float* amax_out,
+                  void* workspace, int32_t* d_status, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
+    return fail(FOS_ERR_CONFIG, "fused amax + QDQ supports 1x16 blocks with a per-tensor scale");
+  if ((rc = check_shape(M, K, FOS_BLOCK_1X16))) return rc;
+  if (M * K > 0 && (!x || !y)) return fail(FOS_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (!amax_out) return fail(FOS_ERR_INVALID_ARG, "amax_out must be non-NULL");
+  if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(FOS_ERR_ALIGN, "x or y misaligned");
+  if (!aligned(workspace, 8) || !aligned(amax_out, 4) || !aligned(d_status, 4))
+    return fail(FOS_ERR_ALIGN, "workspace/amax/status misaligned");
+  if ((rc = check_device())) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
+  fos::Args1x16<1> a;
+  memset(&a, 0, sizeof a);
+  a.t[0] = fos::TensorRef{x, y, nullptr, M, K > 0 ? K : 16, 0};
+  a.n = 1;
+  const int64_t ub = fos::unit_blocks(fos::kOutQdq, dtype);
+  a.total_units = (M * (K / 16) + ub - 1) / ub;
+  a.six_b = six_b(cfg);
+  a.status = d_status;
+  bool done = false;
+  if ((rc = launch_status(fos::launch_fused_qdq(dtype, cfg->recipe, metric, prec, order, a,
+                                                static_cast<uint32_t*>(workspace), amax_out, &done, s))))
+    return rc;
+  if (done) return FOS_OK;
+  // too large for one read: the amax, then the QDQ with it
+  if ((rc = fos_amax(x, dtype, M, K, FOS_AMAX_TENSOR, amax_out, stream))) return rc;
+  return fos_qdq(x, dtype, M, K, amax_out, cfg, y, stream);
+}
+
 int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
                                const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
                                float* group_sdec_out, void* workspace, int32_t* d_status, void* stream) {

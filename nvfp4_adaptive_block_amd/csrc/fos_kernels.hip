@@ -1439,17 +1439,25 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
 
 // ------------------------------------------------------------ on-chip fused amax + quantize
 
-// The fused amax and quantize for a tensor that fits on chip: when no wave
-// has more than kOnchipUnits units, each wave reads its units once, the
-// first kOnchipLds of them straight into a wave-private LDS stage (direct
-// buffer loads: lane l's 16-byte piece k of a unit lands at
-// stage + 1024 k + 16 l) and the rest into registers, takes their
+// The fused amax and quantize (or quantize-dequantize) for a tensor that
+// fits on chip: when no wave has more than onchip_units() units, each wave
+// reads its units once, the first half of them straight into a wave-private
+// LDS stage (direct buffer loads: lane l's 16-byte piece k of the stage
+// lands at stage + 1024 k + 16 l) and the rest into registers, takes their
 // NaN-dropping max, passes the grid barrier of k_fused, and quantizes from
 // the stage and the registers. Phase 2 reads nothing from memory, so the
 // launch moves each input byte once (k_fused reads it twice).
-constexpr int kOnchipLds = 2;  // units per wave staged in LDS
-constexpr int kOnchipReg = 2;  // units per wave held in registers
-constexpr int kOnchipUnits = kOnchipLds + kOnchipReg;
+//
+// A lane holds 128 bytes of input on chip: 8 pieces of 16 bytes in the
+// stage (8 KiB per wave, 32 KiB per workgroup) and 8 in registers.
+constexpr int kOnchipPieces = 8;  // 16-byte pieces per lane, in LDS and again in registers
+
+// 16-byte pieces of a lane's part of one unit
+__host__ __device__ constexpr int unit_pieces(int out, int dt) {
+  return unit_blocks(out, dt) / 64 * (dt == kFP32 ? 4 : 2);
+}
+// units a wave holds on chip (half staged in LDS, half in registers)
+__host__ __device__ constexpr int onchip_units(int out, int dt) { return 2 * kOnchipPieces / unit_pieces(out, dt); }
 
 // Piece k (16 bytes) of a lane's part of a quantize unit: its byte offset in
 // the unit, and the register it is held in (16-bit types: two blocks of two
@@ -1494,13 +1502,16 @@ struct PieceMax {
   }
 };
 
-template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int OUT>
 __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, uint32_t* workspace, float* amax_out) {
-  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  constexpr int kUB = unit_blocks(OUT, DT);
   constexpr int kNB = kUB / 64;
   constexpr int kB = Raw<DT>::kBytes;
-  constexpr int kPieces = kNB * kB / 16;
+  constexpr int kPieces = unit_pieces(OUT, DT);
+  constexpr int kOnchipLds = kOnchipPieces / kPieces;  // units per wave staged in LDS
+  constexpr int kOnchipReg = kOnchipLds;               // units per wave held in registers
   static_assert(sizeof(Raw<DT>) * kNB == 16 * kPieces, "a lane's unit is kPieces 16-byte pieces");
+  static_assert(kOnchipLds * kPieces == kOnchipPieces, "whole units in the stage");
   __shared__ float lds[4][256];
   __shared__ v4i stage[4][kOnchipLds][kPieces][64];
   __shared__ uint32_t part[4];
@@ -1511,12 +1522,12 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   const Table tab{lds[wv], lds[wv] + 128};
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (args.total_units + nwaves - 1) / nwaves;  // <= kOnchipUnits (the launch checks)
+  const int64_t per = (args.total_units + nwaves - 1) / nwaves;  // <= onchip_units (the launch checks)
   const int64_t u = min(args.total_units, wave * per);
   const int64_t u_end = min(args.total_units, u + per);
   const TensorRef& T = args.t[0];
   const int64_t nblk = T.M * (T.K >> 4);
-  const Walk<DT, kGranTensor, kOutQuant> W(T, args.codes, args.scales);
+  const Walk<DT, kGranTensor, OUT> W(T, args.codes, args.scales);
 
   // phase 1: read every unit once; units past the wave's range have empty
   // resources (their loads read zeros and are never used)
@@ -1569,7 +1580,7 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
     if (args.sdec_out) args.sdec_out[0] = 1.0f / global_encode_scale(A, args.six_b);
   }
 
-  // phase 2: quantize the register units, then the staged ones
+  // phase 2: the register units, then the staged ones
   if (u >= u_end) return;
   const float S_enc = global_encode_scale(A, args.six_b);
   const float S_dec = 1.0f / S_enc;
@@ -1578,7 +1589,7 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   for (int r = 0; r < kOnchipReg; r++) {
     const int64_t v = u + kOnchipLds + r;
     if (v < u_end)
-      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, kOutQuant>(R[r], S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
+      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, OUT>(R[r], S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
   }
 #pragma unroll
   for (int t = 0; t < kOnchipLds; t++) {
@@ -1587,7 +1598,7 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
       Raw<DT> q[kNB];
 #pragma unroll
       for (int k = 0; k < kPieces; k++) piece<DT>(q, k) = stage[wv][t][k][lane];
-      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, kOutQuant>(q, S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
+      unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, OUT>(q, S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
     }
   }
 }
@@ -1733,14 +1744,14 @@ template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT
 static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax_out, hipStream_t s) {
   static_assert(GRAN == kGranTensor && OUT == kOutQuant, "fused: per-tensor quantize only");
   auto* fn = &k_fused<DT, RECIPE, METRIC, PREC, ORDER>;
-  auto* fn_chip = &k_fused_onchip<DT, RECIPE, METRIC, PREC, ORDER>;
+  auto* fn_chip = &k_fused_onchip<DT, RECIPE, METRIC, PREC, ORDER, kOutQuant>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
   static const int64_t resident_chip = resident_grid(reinterpret_cast<const void*>(fn_chip));
   // the on-chip form when its resident grid leaves each wave at most
-  // kOnchipUnits units (the tensor then fits in the waves' registers and
+  // onchip_units units (the tensor then fits in the waves' registers and
   // LDS stages), else the two-read form
   const int64_t grid_chip = max((int64_t)1, min(resident_chip, (a.total_units + 3) / 4));
-  const bool chip = a.total_units <= grid_chip * 4 * kOnchipUnits;
+  const bool chip = a.total_units <= grid_chip * 4 * onchip_units(kOutQuant, DT);
   const int64_t grid = chip ? grid_chip : max((int64_t)1, min(resident, (a.total_units + 3) / 4));
   Args1x16<1> args = a;
   void* params[] = {&args, &ws, &amax_out};
@@ -1748,6 +1759,22 @@ static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax
   // A plain launch: a cooperative one costs about 16 us more per call on
   // this device. The grid holds only the workgroups that fit at once, so on
   // a GPU without other long-running work all of them are resident.
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
+}
+
+// Fused amax + QDQ: the on-chip form only; *done is false (and nothing is
+// launched) when the tensor does not fit, and the caller then runs the amax
+// and the QDQ as two launches.
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
+static hipError_t launch_fused_qdq_t(const Args1x16<1>& a, uint32_t* ws, float* amax_out, bool* done, hipStream_t s) {
+  static_assert(GRAN == kGranTensor && OUT == kOutQdq, "fused QDQ: per-tensor scale");
+  auto* fn = &k_fused_onchip<DT, RECIPE, METRIC, PREC, ORDER, kOutQdq>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  *done = a.total_units <= grid * 4 * onchip_units(kOutQdq, DT);
+  if (!*done) return hipSuccess;
+  Args1x16<1> args = a;
+  void* params[] = {&args, &ws, &amax_out};
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 
@@ -1831,6 +1858,13 @@ hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int order
 hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                         float* amax_out, hipStream_t s) {
   FOS_DTYPES(FOS_MODES, kGranTensor, kOutQuant, CALL_F)
+}
+
+#define CALL_FQ(DT, R, M, P, O, G, OUT) launch_fused_qdq_t<DT, R, M, P, O, G, OUT>(a, ws, amax_out, done, s)
+
+hipError_t launch_fused_qdq(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
+                            float* amax_out, bool* done, hipStream_t s) {
+  FOS_DTYPES(FOS_MODES, kGranTensor, kOutQdq, CALL_FQ)
 }
 
 #define CALL_FG(DT, R, M, P, O, G, OUT) launch_fused_grouped_t<DT, R, M, P, O, G, OUT>(a, ws, amax_out, s)

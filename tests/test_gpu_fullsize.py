@@ -228,6 +228,31 @@ def test_fused_at_the_one_read_capacity(orc, dtype, M, K):
     assert not ws[256:].any()
 
 
+@pytest.mark.parametrize("dtype,M,K", [("bf16", 8192, 4096), ("bf16", 8192, 4112), ("fp32", 4096, 4096),
+                                       ("fp32", 4096, 4112)])
+def test_qdq_fused_at_the_one_read_capacity(orc, dtype, M, K):
+    """The fused amax + QDQ right at the capacity of its one-read launch and
+    just past it (K = 4112: the amax launch, then the QDQ launch); sampled
+    rows against the oracle's QDQ with the oracle's amax."""
+    x = synthdata.activation_family("outlier", M, K, 29, dtype)
+    bits = raw_bits(x)
+    xd = x.to("cuda")
+    a = orc.amax(bits, dtype, "tensor")
+    rows = sample_rows(M, 32, 29)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for recipe, metric, prec in (("4over6", "mse", "fp16"), ("4over6", "mae", "exact"), ("nvfp4", "mse", "exact")):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec)
+        y, amax = fos.fos_qdq_fused(xd, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        got = raw_bits(y.cpu())[rows]
+        want = orc.qdq(bits[rows], dtype, a, **kw)
+        if dtype == "fp32":  # compare bits (signed zeros included)
+            got, want = got.view(np.uint32), want.view(np.uint32)
+        np.testing.assert_array_equal(got, want, err_msg=f"{kw}")
+    assert not ws[256:].any()
+
+
 def test_fused_beyond_one_read_16384x4096(orc):
     """A tensor too large for the one-read fused form (twice the dense
     activation tensor) takes the two-read form; sampled rows against the

@@ -496,6 +496,45 @@ def test_fused_stage_lanes_past_the_end(orc):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_qdq_fused(orc, dtype):
+    """The per-tensor amax and the fused QDQ in one launch equal the oracle's
+    amax followed by its QDQ, for every mode and bound, ragged and empty
+    shapes included; the workspace's counters come back zero."""
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for (M, K), family in FUSED_CASES + [((48, 272), "weight")]:
+        x = _family(family, dtype, M, K, 63) if M else torch.empty(0, K, dtype=synthdata.TORCH_DTYPES[dtype])
+        b = raw_bits(x)
+        want_amax = orc.amax(b, dtype, "tensor")
+        for (recipe, metric, prec), bound in itertools.product(MODES, (448, 256)):
+            kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound)
+            y, amax = fos.fos_qdq_fused(dev(x), workspace=ws, status=status, **kw)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), want_amax.view(np.uint32))
+            np.testing.assert_array_equal(u_bits(bits_of(y)), u_bits(orc.qdq(b, dtype, want_amax, **kw)),
+                                          err_msg=f"{M}x{K} {kw}")
+            assert not ws[256:].any(), "the workspace's counters must be zero after a call"
+    assert int(status.item()) == 0
+
+
+def test_qdq_fused_stage_lanes_past_the_end(orc):
+    """As for the fused quantize: stage lanes past a ragged tensor's end hold
+    an earlier launch's values, which must not count in the amax."""
+    big = (synthdata.normal(512, 4096, 83, "bf16").to(torch.float32) * 1e30).to(torch.bfloat16)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for dtype, (M, K) in (("bf16", (67, 1552)), ("fp32", (5, 208)), ("fp16", (33, 4112))):
+        fos.fos_qdq_fused(dev(big), workspace=ws, recipe="4over6")
+        x = synthdata.normal(M, K, 84, dtype)
+        b = raw_bits(x)
+        a = orc.amax(b, dtype, "tensor")
+        y, amax = fos.fos_qdq_fused(dev(x), workspace=ws, recipe="4over6", err_prec="fp16")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32), err_msg=dtype)
+        np.testing.assert_array_equal(u_bits(bits_of(y)), u_bits(orc.qdq(b, dtype, a, recipe="4over6", err_prec="fp16")),
+                                      err_msg=dtype)
+
+
 def test_fused_nan_inf_tensors(orc):
     """NaN-dropping amax inside the fused launch: scattered NaN, an all-NaN
     tensor (amax 0, S_enc 1) and an infinite element (S_enc 1)."""
