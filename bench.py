@@ -38,7 +38,7 @@ PEAK_VALU_LANE_TPS = 256 * 64 * 2.4e9  # VALU lane-instructions/s: 256 CUs x 64 
 MALL_BYTES = 256 << 20
 FOOTPRINT = 1 << 30            # rotate buffers up to >= 1 GiB
 METRIC = "4over6 quantize/QDQ achieved HBM GB/s and % of MI355X peak (bit-exact)"
-FUSED_KERNEL = "void fos::k_fused_onchip<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)"
+FUSED_KERNEL = "void fos::k_fused_onchip<0, 1, 1, 0, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)"
 QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0, 0>(fos::Args1x16<1>)"
 COPY_BYTES = 256 << 20         # the profile pass's calibration copy
 # counter summaries per kernel: (file, readable workload, algorithmic bytes per launch)
@@ -312,7 +312,7 @@ def main():
 
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o kt -- "
-          "python3 $REPO/bench.py --steps 200 --warmup 20 --no-cpu-baseline",
+          "python3 $REPO/bench.py --steps 200 --no-cpu-baseline",
     "fetch": "timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o fetch -- "
              "python3 $REPO/bench.py --profile-pass",
     "write": "timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o write -- "
@@ -346,12 +346,12 @@ def describe_kernel(name: str) -> str:
         dt, rc, mt, pr, gr, out = m.groups()
         err = f" {_MT[mt]} {_PR[pr]}" if rc == "1" else ""
         return f"16x16 {_OUT[out]} {_DT[dt]} {_RC[rc]}{err} {_GR[gr]}"
-    m = re.match(r"void fos::k_fused(_onchip)?<(\d), (\d), (\d), (\d), (\d)>", name)
+    m = re.match(r"void fos::k_fused(_onchip)?<(\d), (\d), (\d), (\d), (\d)(?:, (\d))?>", name)
     if m:
-        form, dt, rc, mt, pr, od = m.groups()
+        form, dt, rc, mt, pr, od, out = m.groups()
         err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
         form = " (one read)" if form else " (two reads)"
-        return f"fused amax + 1x16 quantize{form} {_DT[dt]} {_RC[rc]}{err} tensor"
+        return f"fused amax + 1x16 {_OUT[out or '0']}{form} {_DT[dt]} {_RC[rc]}{err} tensor"
     m = re.match(r"void fos::k_fused_grouped<(\d), (\d), (\d), (\d), (\d)>", name)
     if m:
         dt, rc, mt, pr, od = m.groups()

@@ -38,6 +38,8 @@ def test_kernel_descriptions():
     assert d("void fos::k_1x16<48, 1, 1, 0, 1, 1, 0, 1>(fos::Args1x16<48>)") == \
         "1x16 qdq list<48> fp16 4over6 mae fp16err seq tensor"
     assert d(bench.FUSED_KERNEL) == "fused amax + 1x16 quantize (one read) bf16 4over6 mse exact tensor"
+    assert d("void fos::k_fused_onchip<1, 1, 0, 1, 0, 1>(fos::Args1x16<1>, unsigned int*, float*)") == \
+        "fused amax + 1x16 qdq (one read) fp16 4over6 mae fp16err tensor"
     assert d("void fos::k_fused<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)") == \
         "fused amax + 1x16 quantize (two reads) bf16 4over6 mse exact tensor"
     assert d("void fos::k_16x16<2, 1, 1, 0, 1, 0>(fos::Args16x16)").startswith("16x16 quantize fp32 4over6")
