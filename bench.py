@@ -504,7 +504,20 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
     out["quantize_1x16_bf16_8192x4096_per_row_amax"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
                                                         "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
     log(f"[bench] quantize bf16 8192x4096, per-row amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
-    del row_amax
+    # per-row amaxes computed on the device: one launch (each row read from
+    # HBM once), against fos_amax per row followed by fos_quantize
+    ra = torch.empty(xs[0].shape[0], dtype=torch.float32, device="cuda")
+    for key, fn in (("fused_row_amax_quantize_bf16_8192x4096",
+                     lambda i: fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=ra, sdec=rsdec,
+                                                      **rknobs)),
+                    ("row_amax_then_quantize_bf16_8192x4096",
+                     lambda i: (fos.fos_amax(xs[i], "row", out=ra),
+                                fos.fos_quantize(xs[i], ra, codes=codes[i], scales=scales[i], sdec=rsdec, **rknobs)))):
+        _, ms = time_loop(fn, len(xs), 200, 10)
+        avg = float(np.median(ms))
+        out[key] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg), "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
+        log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s (x read once + codes and scales)")
+    del row_amax, ra
 
     # fused fake quantization of the same tensor with its amax computed on
     # the device: one launch that reads x once, against fos_amax + fos_qdq

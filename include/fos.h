@@ -220,10 +220,14 @@ int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, cons
  * Megatron-LM PR runs as a separate FP32 torch reduction ("What does this PR
  * do?", fused data path) folded into the quantizer of the pytorch/ao PR
  * (recipe commit). The result equals fos_amax(..., FOS_AMAX_TENSOR) followed
- * by fos_quantize with that amax, bit for bit. cfg must be 1x16 with
- * FOS_PER_TENSOR.
- *   amax_out:  nullable device float[1], receives the NaN-dropping max |x|.
- *   sdec_out:  nullable device float[1], receives S_dec.
+ * by fos_quantize with that amax, bit for bit. cfg must be 1x16.
+ * With cfg->scale_gran FOS_PER_ROW (added in ABI version 4) the amax is per
+ * row: the result equals fos_amax(..., FOS_AMAX_ROW) followed by
+ * fos_quantize with those amaxes; that form has no grid-wide step and does
+ * not use the workspace (which must still be passed).
+ *   amax_out:  nullable device float[1] (per row: [M]), receives the
+ *              NaN-dropping max |x|.
+ *   sdec_out:  nullable device float[1] (per row: [M]), receives S_dec.
  *   workspace: device memory of FOS_FUSED_WORKSPACE_BYTES, 8-byte aligned,
  *              all zero before its first use (e.g. cleared once at
  *              allocation). Every completed call leaves its counters zero

@@ -167,20 +167,22 @@ def fused_workspace(device) -> torch.Tensor:
 
 def fos_quantize_fused(x: torch.Tensor, *, codes=None, scales=None, amax=None, sdec=None, status=None,
                        workspace=None, **knobs):
-    """Per-tensor amax and quantize in one launch. Returns (codes, scales,
-    amax float32[1], sdec float32[1])."""
+    """Amax (per tensor, or per row with scale_gran="row") and quantize in
+    one launch. Returns (codes, scales, amax float32[1 or M], sdec float32[1
+    or M])."""
     _need(x, "x")
     M, K = x.shape
     cfg = config(**knobs)
     dev = x.device
+    n_amax = M if knobs.get("scale_gran", "tensor") == "row" else 1
     if codes is None:
         codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
     if amax is None:
-        amax = torch.empty(1, dtype=torch.float32, device=dev)
+        amax = torch.empty(n_amax, dtype=torch.float32, device=dev)
     if sdec is None:
-        sdec = torch.empty(1, dtype=torch.float32, device=dev)
+        sdec = torch.empty(n_amax, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = fused_workspace(dev)
     with torch.cuda.device(dev):

@@ -359,8 +359,8 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   int rc;
   if ((rc = check_dtype(dtype))) return rc;
   if ((rc = check_cfg(cfg))) return rc;
-  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
-    return fail(FOS_ERR_CONFIG, "fused amax + quantize supports 1x16 blocks with a per-tensor scale");
+  if (cfg->block != FOS_BLOCK_1X16)
+    return fail(FOS_ERR_CONFIG, "fused amax + quantize supports 1x16 blocks");
   if ((rc = check_shape(M, K, FOS_BLOCK_1X16))) return rc;
   if (M * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
   if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
@@ -375,12 +375,17 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   a.t[0] = fos::TensorRef{x, nullptr, nullptr, M, K > 0 ? K : 16, 0};
   a.n = 1;
   const int64_t ub = fos::unit_blocks(fos::kOutQuant, dtype);
-  a.total_units = (M * (K / 16) + ub - 1) / ub;
   a.six_b = six_b(cfg);
   a.codes = codes;
   a.scales = scales;
   a.sdec_out = sdec_out;
   a.status = d_status;
+  if (cfg->scale_gran == FOS_PER_ROW) {  // per-row segments, one wave per row at a time
+    a.total_units = M * ((a.t[0].K / 16 + ub - 1) / ub);
+    return launch_status(fos::launch_fused_row(dtype, cfg->recipe, metric, prec, order, a, amax_out,
+                                               static_cast<hipStream_t>(stream)));
+  }
+  a.total_units = (M * (K / 16) + ub - 1) / ub;
   return launch_status(fos::launch_fused(dtype, cfg->recipe, metric, prec, order, a, static_cast<uint32_t*>(workspace),
                                          amax_out, static_cast<hipStream_t>(stream)));
 }

@@ -88,6 +88,8 @@ hipError_t launch_quant_1x16(int dt, int recipe, int metric, int prec, int order
                              hipStream_t s);
 hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                         float* amax_out, hipStream_t s);
+hipError_t launch_fused_row(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a,
+                            float* amax_out, hipStream_t s);
 hipError_t launch_fused_qdq(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                             float* amax_out, bool* done, hipStream_t s);
 hipError_t launch_fused_grouped(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a,

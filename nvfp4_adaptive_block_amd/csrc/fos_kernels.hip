@@ -533,11 +533,11 @@ __device__ __forceinline__ void unit_1x16(const Raw<DT>* raw, float S_enc, float
 
 // The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED the
 // amaxes come from `fused_amax` (LDS, as float bits) rather than from
-// memory: [1] for a per-tensor scale, [G] for grouped scales.
+// memory: [1] for a per-tensor scale, [G] for grouped scales, and for
+// per-row scales [1], the amax of the one row the range covers.
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT, bool FUSED>
 __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
                                           int64_t u_end, const uint32_t* fused_amax) {
-  static_assert(!FUSED || GRAN != kGranRow, "fused amaxes: per tensor or per group");
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kNB = unit_blocks(OUT, DT) / 64;
   const int64_t total = args.total_units;
@@ -576,7 +576,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
         if (valid && row != tab_row) {
           float A;
           if (GRAN == kGranRow) {
-            A = ld_const(T.amax, row);
+            A = FUSED ? __uint_as_float(fused_amax[0]) : ld_const(T.amax, row);
           } else {
             if (row < g_lo || row >= g_hi) {
               g_cur = group_of(args.offs, args.G, row);
@@ -1603,6 +1603,41 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   }
 }
 
+// ------------------------------------------------------------ fused per-row amax + quantize
+
+// Per-row global scales need no grid-wide step: each wave takes whole rows
+// (row w, w + nwaves, ...), reads a row once for its NaN-dropping max,
+// writes the row's amax and S_dec, and quantizes the row with the 1x16
+// walk. The walk's loads re-read the row the wave has just read, from the
+// L2 cache, so each byte of x crosses HBM about once.
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
+__global__ void __launch_bounds__(256) k_fused_row(const Args1x16<1> args, float* amax_out) {
+  __shared__ float lds[4][256];
+  __shared__ uint32_t row_amax[4];
+  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const TensorRef& T = args.t[0];
+  const int64_t nbk = T.K >> 4, spr = (nbk + kUB - 1) / kUB;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wv; r < T.M; r += nwaves) {
+    const uint32_t m = wave_max_u32(range_absmax<DT>(T.x, r * nbk, (r + 1) * nbk, lane));
+    const float A = __uint_as_float(m);
+    if (lane == 0) {
+      row_amax[wv] = m;
+      if (amax_out) amax_out[r] = A;
+      if (args.sdec_out) args.sdec_out[r] = 1.0f / global_encode_scale(A, args.six_b);
+    }
+    // the lanes read the word lane 0 wrote
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranRow, kOutQuant, true>(args, tab, lane, r * spr, (r + 1) * spr,
+                                                                            &row_amax[wv]);
+  }
+}
+
 // Grouped (MoE) amax and quantize in one launch: the per-group amaxes the
 // grouped quantize takes as input (pytorch/ao PR, MoE commit) computed in
 // phase 1 of the same launch. Each wave takes the NaN-dropping max over the
@@ -1762,6 +1797,16 @@ static hipError_t launch_fused_t(const Args1x16<1>& a, uint32_t* ws, float* amax
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
+static hipError_t launch_fused_row_t(const Args1x16<1>& a, float* amax_out, hipStream_t s) {
+  static_assert(GRAN == kGranRow && OUT == kOutQuant, "fused per-row: quantize");
+  auto* fn = &k_fused_row<DT, RECIPE, METRIC, PREC, ORDER>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t grid = max((int64_t)1, min(resident, (a.t[0].M + 3) / 4));
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a, amax_out);
+  return hipGetLastError();
+}
+
 // Fused amax + QDQ: the on-chip form only; *done is false (and nothing is
 // launched) when the tensor does not fit, and the caller then runs the amax
 // and the QDQ as two launches.
@@ -1861,6 +1906,12 @@ hipError_t launch_fused(int dt, int recipe, int metric, int prec, int order, con
 }
 
 #define CALL_FQ(DT, R, M, P, O, G, OUT) launch_fused_qdq_t<DT, R, M, P, O, G, OUT>(a, ws, amax_out, done, s)
+#define CALL_FR(DT, R, M, P, O, G, OUT) launch_fused_row_t<DT, R, M, P, O, G, OUT>(a, amax_out, s)
+
+hipError_t launch_fused_row(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a,
+                            float* amax_out, hipStream_t s) {
+  FOS_DTYPES(FOS_MODES, kGranRow, kOutQuant, CALL_FR)
+}
 
 hipError_t launch_fused_qdq(int dt, int recipe, int metric, int prec, int order, const Args1x16<1>& a, uint32_t* ws,
                             float* amax_out, bool* done, hipStream_t s) {

@@ -253,6 +253,26 @@ def test_qdq_fused_at_the_one_read_capacity(orc, dtype, M, K):
     assert not ws[256:].any()
 
 
+@pytest.mark.parametrize("family", ["outlier", "special"])
+def test_fused_row_dense_activation_8192x4096(orc, family):
+    """The fused per-row amax + quantize on the full dense activation tensor
+    (the special family's first rows are all zero); the amaxes in full,
+    sampled rows against the oracle."""
+    M, K = 8192, 4096
+    x = synthdata.activation_family(family, M, K, 24, "bf16")
+    bits = raw_bits(x)
+    a = orc.amax(bits, "bf16", "row")
+    rows = sample_rows(M, 48, 24, extra=range(8))
+    for recipe, metric, prec in (("4over6", "mse", "exact"), ("4over6", "mae", "fp16"), ("nvfp4", "mse", "exact")):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, scale_gran="row")
+        codes, scales, amax, _ = fos.fos_quantize_fused(x.to("cuda"), **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+        want = orc.quantize(bits[rows], "bf16", a[rows], **kw)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"], err_msg=f"{kw}")
+        np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"{kw}")
+
+
 def test_fused_beyond_one_read_16384x4096(orc):
     """A tensor too large for the one-read fused form (twice the dense
     activation tensor) takes the two-read form; sampled rows against the

@@ -535,6 +535,33 @@ def test_qdq_fused_stage_lanes_past_the_end(orc):
                                       err_msg=dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_fused_row_amax_quantize(orc, dtype):
+    """Per-row amaxes and the quantize in one launch equal the oracle's
+    per-row amax followed by its per-row quantize, for every mode and bound:
+    rows of zeros, a row of NaN, an infinite element, ragged and long rows."""
+    cases = [((67, 1552), "outlier"), ((96, 1040), "special"), ((1, 16), "normal"), ((5, 14336), "normal"),
+             ((0, 64), "normal")]
+    for (M, K), family in cases:
+        x = _family(family, dtype, M, K, 65) if M else torch.empty(0, K, dtype=synthdata.TORCH_DTYPES[dtype])
+        if M >= 67:
+            t = x.to(torch.float32)
+            t[10, :] = float("nan")
+            t[20, 3] = float("inf") if dtype != "fp16" else 60000.0
+            x = t.to(synthdata.TORCH_DTYPES[dtype])
+        b = raw_bits(x)
+        want_amax = orc.amax(b, dtype, "row")
+        for (recipe, metric, prec), bound in itertools.product(MODES, (448, 256)):
+            kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, scale_gran="row")
+            codes, scales, amax, sdec = fos.fos_quantize_fused(dev(x), **kw)
+            torch.cuda.synchronize()
+            want = orc.quantize(b, dtype, want_amax, **kw)
+            np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), want_amax.view(np.uint32))
+            np.testing.assert_array_equal(sdec.cpu().numpy().view(np.uint32), want["sdec"].view(np.uint32))
+            np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{M}x{K} {kw}")
+            np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{M}x{K} {kw}")
+
+
 def test_fused_nan_inf_tensors(orc):
     """NaN-dropping amax inside the fused launch: scattered NaN, an all-NaN
     tensor (amax 0, S_enc 1) and an infinite element (S_enc 1)."""
