@@ -352,6 +352,11 @@ def describe_kernel(name: str) -> str:
         err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
         form = " (one read)" if form else " (two reads)"
         return f"fused amax + 1x16 {_OUT[out or '0']}{form} {_DT[dt]} {_RC[rc]}{err} tensor"
+    m = re.match(r"void fos::k_fused_row<(\d), (\d), (\d), (\d), (\d)>", name)
+    if m:
+        dt, rc, mt, pr, od = m.groups()
+        err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
+        return f"fused per-row amaxes + 1x16 quantize {_DT[dt]} {_RC[rc]}{err} row"
     m = re.match(r"void fos::k_fused_grouped<(\d), (\d), (\d), (\d), (\d)>", name)
     if m:
         dt, rc, mt, pr, od = m.groups()

@@ -44,6 +44,8 @@ def test_kernel_descriptions():
         "fused amax + 1x16 quantize (two reads) bf16 4over6 mse exact tensor"
     assert d("void fos::k_16x16<2, 1, 1, 0, 1, 0>(fos::Args16x16)").startswith("16x16 quantize fp32 4over6")
     assert "grouped" in d("void fos::k_fused_grouped<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)")
+    assert d("void fos::k_fused_row<0, 1, 1, 0, 0>(fos::Args1x16<1>, float*)") == \
+        "fused per-row amaxes + 1x16 quantize bf16 4over6 mse exact row"
     assert d("void fos::k_colwise<0, 1, 1, 0, 0>(fos::Args16x16)").startswith("columnwise")
     assert d("void fos::k_dequant<0, 0>(unsigned char const*)") == "dequantize to bf16 tensor"
     assert d("some_other_kernel") == ""
