@@ -40,6 +40,31 @@ def test_host_only_calls():
     assert rc != 0
 
 
+def test_fused_calls_validate_before_touching_a_device():
+    """The fused entry points' argument checks run on the host and return
+    their error codes before any device call (fake, never-dereferenced
+    addresses stand in for device buffers)."""
+    lib = fos.load_library()
+    P = ctypes.c_void_p
+    x, y, ws, a = P(0x10000), P(0x20000), P(0x30000), P(0x40000)
+    cfg = fos.config(recipe="4over6")
+    tiles = fos.config(recipe="4over6", block="16x16")
+    rows = fos.config(recipe="4over6", scale_gran="row")
+    # fos_qdq_fused: 1x16 with a per-tensor scale only; y, amax_out and workspace required; 8-byte workspace
+    assert lib.fos_qdq_fused(x, 0, 16, 64, ctypes.byref(tiles), y, a, ws, None, None) == 5   # FOS_ERR_CONFIG
+    assert lib.fos_qdq_fused(x, 0, 16, 64, ctypes.byref(rows), y, a, ws, None, None) == 5
+    assert lib.fos_qdq_fused(x, 0, 16, 40, ctypes.byref(cfg), y, a, ws, None, None) == 3     # FOS_ERR_SHAPE
+    assert lib.fos_qdq_fused(x, 0, 16, 64, ctypes.byref(cfg), y, None, ws, None, None) == 1  # amax_out NULL
+    assert lib.fos_qdq_fused(x, 0, 16, 64, ctypes.byref(cfg), y, a, None, None, None) == 1   # workspace NULL
+    assert lib.fos_qdq_fused(x, 0, 16, 64, ctypes.byref(cfg), y, a, P(0x30004), None, None) == 4  # FOS_ERR_ALIGN
+    assert lib.fos_qdq_fused(x, 0, 16, 64, ctypes.byref(cfg), P(0x20008), a, ws, None, None) == 4
+    # fos_quantize_fused: 16x16 is rejected; per-row passes the argument checks
+    codes, scales = P(0x50000), P(0x60000)
+    assert lib.fos_quantize_fused(x, 0, 16, 64, ctypes.byref(tiles), codes, scales, a, None, ws, None, None) == 5
+    rc = lib.fos_quantize_fused(x, 0, 16, 64, ctypes.byref(rows), codes, scales, a, None, P(0x30004), None, None)
+    assert rc == 4, "per-row is accepted up to the workspace alignment check"
+
+
 def test_product_package_does_not_reach_the_oracle():
     """The product path imports, includes and links nothing under oracle/."""
     pkg = os.path.join(ROOT, "nvfp4_adaptive_block_amd")
