@@ -1606,36 +1606,102 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
 // ------------------------------------------------------------ fused per-row amax + quantize
 
 // Per-row global scales need no grid-wide step: each wave takes whole rows
-// (row w, w + nwaves, ...), reads a row once for its NaN-dropping max,
-// writes the row's amax and S_dec, and quantizes the row with the 1x16
-// walk. The walk's loads re-read the row the wave has just read, from the
-// L2 cache, so each byte of x crosses HBM about once.
+// (row w, w + nwaves, ...), takes a row's NaN-dropping max, writes the row's
+// amax and S_dec, and quantizes the row.
+//
+// A row of at most kRowStage units (8 KiB: bf16 and fp16 up to K = 4096,
+// fp32 up to 2048) is read once, into a wave-private LDS stage with direct
+// buffer loads; the wave copies it to registers, starts the next row's loads
+// into the stage, and takes the amax and the quantize from the registers, so
+// the next row's read overlaps this row's compute. A longer row is read for
+// its max and then quantized with the 1x16 walk, whose loads find the row
+// in the L2 cache.
 template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
 __global__ void __launch_bounds__(256) k_fused_row(const Args1x16<1> args, float* amax_out) {
+  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  constexpr int kNB = kUB / 64;
+  constexpr int kPieces = unit_pieces(kOutQuant, DT);
+  constexpr int kRowStage = kOnchipPieces / kPieces;  // units of a row the stage holds
   __shared__ float lds[4][256];
   __shared__ uint32_t row_amax[4];
-  constexpr int kUB = unit_blocks(kOutQuant, DT);
+  __shared__ v4i stage[4][kRowStage][kPieces][64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const Table tab{lds[wv], lds[wv] + 128};
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const TensorRef& T = args.t[0];
   const int64_t nbk = T.K >> 4, spr = (nbk + kUB - 1) / kUB;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + wv; r < T.M; r += nwaves) {
-    const uint32_t m = wave_max_u32(range_absmax<DT>(T.x, r * nbk, (r + 1) * nbk, lane));
+  const float six_b = args.six_b;
+  const int64_t r0 = (int64_t)blockIdx.x * 4 + wv;
+
+  auto publish = [&](int64_t r, uint32_t m) {
     const float A = __uint_as_float(m);
     if (lane == 0) {
-      row_amax[wv] = m;
       if (amax_out) amax_out[r] = A;
-      if (args.sdec_out) args.sdec_out[r] = 1.0f / global_encode_scale(A, args.six_b);
+      if (args.sdec_out) args.sdec_out[r] = 1.0f / global_encode_scale(A, six_b);
     }
-    // the lanes read the word lane 0 wrote
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranRow, kOutQuant, true>(args, tab, lane, r * spr, (r + 1) * spr,
-                                                                            &row_amax[wv]);
+  };
+
+  if (spr > kRowStage) {
+    for (int64_t r = r0; r < T.M; r += nwaves) {
+      const uint32_t m = wave_max_u32(range_absmax<DT>(T.x, r * nbk, (r + 1) * nbk, lane));
+      publish(r, m);
+      if (lane == 0) row_amax[wv] = m;
+      // the lanes read the word lane 0 wrote
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranRow, kOutQuant, true>(args, tab, lane, r * spr,
+                                                                              (r + 1) * spr, &row_amax[wv]);
+    }
+    return;
   }
+
+  const Walk<DT, kGranRow, kOutQuant> W(T, args.codes, args.scales);
+  auto stage_row = [&](int64_t r) {  // the row's units into the stage (rows past the end: nothing read)
+#pragma unroll
+    for (int t = 0; t < kRowStage; t++) {
+      const Unit U = W.unit(UPos{r * spr + t, r, t}, r < T.M && t < spr, T.M);
+#pragma unroll
+      for (int k = 0; k < kPieces; k++) load_lds16(U.x, &stage[wv][t][k][0], piece_offset<DT>(lane, k));
+    }
+  };
+  stage_row(r0);
+  for (int64_t r = r0; r < T.M; r += nwaves) {
+    Raw<DT> R[kRowStage][kNB];
+    vm_wait();  // the row has landed in the stage
+#pragma unroll
+    for (int t = 0; t < kRowStage; t++)
+#pragma unroll
+      for (int k = 0; k < kPieces; k++) piece<DT>(R[t], k) = stage[wv][t][k][lane];
+    // the copies have left the stage before the next row's loads overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_row(r + nwaves);
+    // NaN-dropping max over the row's blocks: a lane past the row's end
+    // holds whatever an earlier row or launch left in the stage
+    PieceMax<DT> pm;
+    const v4i zero = {0, 0, 0, 0};  // +0: leaves the max unchanged
+#pragma unroll
+    for (int t = 0; t < kRowStage; t++) {
+      const int64_t nvalid = t < spr ? min((int64_t)kUB, nbk - t * kUB) : 0;
+#pragma unroll
+      for (int k = 0; k < kPieces; k++) {
+        const int64_t blk = (DT == kFP32) ? lane : (k >> 1) * 64 + lane;
+        pm.add(blk < nvalid ? piece<DT>(R[t], k) : zero);
+      }
+    }
+    const uint32_t m = wave_max_u32(pm.bits());
+    publish(r, m);
+    const float S_enc = global_encode_scale(__uint_as_float(m), six_b);
+    const float S_dec = 1.0f / S_enc;
+    tab.build(S_enc, S_dec, lane);
+#pragma unroll
+    for (int t = 0; t < kRowStage; t++)
+      if (t < spr)
+        unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, kOutQuant>(R[t], S_enc, S_dec, tab,
+                                                             W.unit(UPos{r * spr + t, r, t}, true, T.M), lane);
+  }
+  vm_wait();  // no stage load outlives the wave
 }
 
 // Grouped (MoE) amax and quantize in one launch: the per-group amaxes the
