@@ -443,6 +443,72 @@ def test_runs_on_a_side_stream(orc):
     np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
 
 
+def test_fused_calls_on_a_side_stream(orc):
+    """The fused entry points launch on the caller's current stream."""
+    x = synthdata.activation_family("outlier", 96, 1040, 10, "bf16")
+    b = raw_bits(x)
+    at, ar = orc.amax(b, "bf16", "tensor"), orc.amax(b, "bf16", "row")
+    s = torch.cuda.Stream()
+    xd = dev(x)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c1, s1, _, _ = fos.fos_quantize_fused(xd, workspace=ws, recipe="4over6")
+        c2, s2, _, _ = fos.fos_quantize_fused(xd, workspace=ws, recipe="4over6", scale_gran="row")
+        y, _ = fos.fos_qdq_fused(xd, workspace=ws, recipe="4over6", err_prec="fp16")
+    s.synchronize()
+    w1 = orc.quantize(b, "bf16", at, recipe="4over6")
+    w2 = orc.quantize(b, "bf16", ar, recipe="4over6", scale_gran="row")
+    np.testing.assert_array_equal(c1.cpu().numpy(), w1["codes"])
+    np.testing.assert_array_equal(s1.cpu().numpy(), w1["scales"])
+    np.testing.assert_array_equal(c2.cpu().numpy(), w2["codes"])
+    np.testing.assert_array_equal(s2.cpu().numpy(), w2["scales"])
+    np.testing.assert_array_equal(bits_of(y), orc.qdq(b, "bf16", at, recipe="4over6", err_prec="fp16"))
+
+
+def test_fused_calls_replay_in_a_graph(orc):
+    """The fused calls allocate nothing and clear nothing with a memset, so a
+    captured graph of them replays correctly: three replays over changing
+    inputs, with eager work and synchronisation between them, each checked
+    against the oracle."""
+    M, K = 64, 1040
+    xd = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    codes = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    sdec = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(xd)
+    qa = torch.empty(1, dtype=torch.float32, device="cuda")
+    xd.copy_(synthdata.normal(M, K, 30, "bf16").to("cuda"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the calls up on the capture stream first
+        fos.fos_quantize_fused(xd, codes=codes, scales=scales, amax=amax, sdec=sdec, workspace=ws, recipe="4over6")
+        fos.fos_qdq_fused(xd, out=y, amax=qa, workspace=ws, recipe="4over6", err_prec="fp16")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fos.fos_quantize_fused(xd, codes=codes, scales=scales, amax=amax, sdec=sdec, workspace=ws, recipe="4over6")
+        fos.fos_qdq_fused(xd, out=y, amax=qa, workspace=ws, recipe="4over6", err_prec="fp16")
+    for seed in (31, 32, 33):
+        x = synthdata.activation_family("outlier", M, K, seed, "bf16")
+        xd.copy_(x.to("cuda"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        b = raw_bits(x)
+        a = orc.amax(b, "bf16", "tensor")
+        want = orc.quantize(b, "bf16", a, recipe="4over6")
+        np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32), err_msg=f"{seed}")
+        np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"{seed}")
+        np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"{seed}")
+        np.testing.assert_array_equal(bits_of(y), orc.qdq(b, "bf16", a, recipe="4over6", err_prec="fp16"),
+                                      err_msg=f"{seed}")
+    assert not ws[256:].any()
+
+
 # ------------------------------------------------------------------ fused amax + quantize
 
 FUSED_CASES = [((67, 1552), "outlier"), ((256, 1024), "normal"), ((1, 16), "special"), ((96, 1040), "special"),
