@@ -485,6 +485,17 @@ def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
     def gbs(nbytes, ms):
         return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
+    # the achievable ceiling in the same run: a plain 256 MiB device-to-device
+    # copy (reads and writes 256 MiB each), four buffer pairs in rotation
+    srcs = [torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    _, ms = time_loop(lambda i: dsts[i].copy_(srcs[i]), len(srcs), 50, 5)
+    avg = float(np.median(ms))
+    out["copy_256MiB_device_to_device"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(2 * COPY_BYTES, avg),
+                                           "frac": round(gbs(2 * COPY_BYTES, avg) / PEAK_HBM_GBS, 4)}
+    log(f"[bench] device copy 256 MiB: {avg * 1e3:.1f} us, {gbs(2 * COPY_BYTES, avg):.0f} GB/s (the ceiling)")
+    del srcs, dsts
+
     # the dense activation tensor: the quantize kernel alone with a
     # precomputed amax (the pages' kernel metric), and the two-launch step
     xs, codes, scales, amax, sdec, knobs = c2
