@@ -273,6 +273,27 @@ def test_fused_row_dense_activation_8192x4096(orc, family):
         np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"], err_msg=f"{kw}")
 
 
+@pytest.mark.parametrize("dtype,M,K", [("bf16", 20000, 512), ("bf16", 300, 4096), ("bf16", 300, 4112),
+                                       ("fp32", 300, 2048), ("fp32", 300, 2064), ("fp16", 5000, 1040)])
+def test_fused_row_stage_limit_and_many_rows(orc, dtype, M, K):
+    """The fused per-row amax + quantize with several rows per wave (the
+    staged rows pipeline into each other) and with rows exactly at the 8 KiB
+    stage (bf16 K = 4096, fp32 K = 2048) and just past it (the read-then-walk
+    form); every amax, and sampled rows, against the oracle."""
+    x = synthdata.activation_family("outlier", M, K, 33, dtype)
+    bits = raw_bits(x)
+    a = orc.amax(bits, dtype, "row")
+    rows = sample_rows(M, 40, 33)
+    kw = dict(recipe="4over6", err_metric="mse", err_prec="exact", scale_gran="row")
+    codes, scales, amax, sdec = fos.fos_quantize_fused(x.to("cuda"), **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+    want = orc.quantize(bits[rows], dtype, a[rows], **kw)
+    np.testing.assert_array_equal(sdec.cpu().numpy()[rows].view(np.uint32), want["sdec"].view(np.uint32))
+    np.testing.assert_array_equal(scales.cpu().numpy()[rows], want["scales"])
+    np.testing.assert_array_equal(codes.cpu().numpy()[rows], want["codes"])
+
+
 def test_fused_beyond_one_read_16384x4096(orc):
     """A tensor too large for the one-read fused form (twice the dense
     activation tensor) takes the two-read form; sampled rows against the
