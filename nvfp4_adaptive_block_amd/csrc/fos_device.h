@@ -78,10 +78,12 @@ __device__ __forceinline__ float global_encode_scale(float A, float six_b) {
   return ok ? s : 1.0f;
 }
 
-// E4M3 code (RNE, saturating at 448) of t >= 0, t not NaN.
+// E4M3 code (RNE, saturating at 448) of t >= 0, t not NaN. The pair
+// convert writes code(t) to byte 0 and code(+0) = 0 to byte 1 of a zero
+// word, so the result needs no mask.
 __device__ __forceinline__ uint32_t e4m3_code(float t) {
   float tc = __builtin_fminf(t, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tc, tc, 0, false) & 0xFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tc, 0.0f, 0, false);
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
@@ -93,7 +95,9 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
 // Eight E2M1 codes (two per byte lane, element 2j in the low nibble) of
 // v[0..7] into one dword. NaN inputs give (sign | 7); see the header note.
 __device__ __forceinline__ uint32_t e2m1_pack8(const float* v) {
-  uint32_t w = 0;
+  // each convert writes one byte of w, so its starting value never shows:
+  // starting from v[0]'s bits lets the first convert write over v[0] in place
+  uint32_t w = __float_as_uint(v[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
