@@ -106,6 +106,37 @@ def test_caller_amax_edge_values(orc):
             assert_quant_equal(orc, x, "fp32", a, label=f"A={A}", recipe=recipe, err_metric=metric, err_prec=prec)
 
 
+
+def test_fp16_error_mode_past_binary16_range(orc):
+    """FP16-error mode where decoded values leave binary16's range: blocks of
+    magnitudes around and past 65504 (x-hat rounds to inf in binary16, so a
+    candidate's error terms turn infinite or NaN), blocks below its subnormal
+    range (x-hat rounds to zero or a subnormal), and ordinary blocks with one
+    huge element; the quantize with per-tensor and per-row scales and the
+    QDQ, bf16 and fp32 inputs, against the oracle."""
+    rng = np.random.default_rng(71)
+    M, K = 48, 272
+    x = np.empty((M, K))
+    x[:16] = rng.uniform(3.0e4, 2.0e5, (16, K))
+    x[16:32] = 10.0 ** rng.uniform(-10, -6, (16, K))
+    x[32:] = rng.standard_normal((16, K))
+    x[32:, ::16] = 1.0e5
+    x = (x * np.where(rng.random((M, K)) < 0.5, -1.0, 1.0)).astype(np.float32)
+    for dtype in ("fp32", "bf16"):
+        xt = torch.from_numpy(x).to(synthdata.TORCH_DTYPES[dtype])
+        b = raw_bits(xt)
+        for gran in ("tensor", "row"):
+            a = orc.amax(b, dtype, gran)
+            for metric in ("mae", "mse"):
+                assert_quant_equal(orc, xt, dtype, a, label=f"{dtype} {gran}", recipe="4over6", err_metric=metric,
+                                   err_prec="fp16", scale_gran=gran)
+        a = orc.amax(b, dtype, "tensor")
+        for metric in ("mae", "mse"):
+            y = fos.fos_qdq(dev(xt), dev(torch.from_numpy(a)), recipe="4over6", err_metric=metric, err_prec="fp16")
+            torch.cuda.synchronize()
+            want = orc.qdq(b, dtype, a, recipe="4over6", err_metric=metric, err_prec="fp16")
+            np.testing.assert_array_equal(u_bits(bits_of(y)), u_bits(want), err_msg=f"qdq {dtype} {metric}")
+
 def test_nan_inf_and_signed_zero_blocks(orc):
     """NaN (quiet and signalling, both signs), +-inf, +-0, subnormals: the
     careful path and the NaN rule (+6)."""
