@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FOS_ABI_VERSION 4
+#define FOS_ABI_VERSION 5
 
 /* element types */
 #define FOS_BF16 0
@@ -109,7 +109,7 @@ extern "C" {
 /* device status bits */
 #define FOS_STATUS_TILE_NONUNIFORM 1 /* 16x16 with a per-row amax that differs within a 16-row band */
 #define FOS_STATUS_BAD_OFFS 2        /* group offsets not monotone, not multiples of 16, or past M_alloc */
-#define FOS_STATUS_BARRIER_TIMEOUT 4 /* fused calls: the grid barrier did not complete (workspace not zero) */
+#define FOS_STATUS_BARRIER_TIMEOUT 4 /* fused calls: the grid barrier did not complete in time (fos_set_barrier_poll_limit) */
 
 /* Bytes of the device workspace the fused calls (fos_quantize_fused,
  * fos_quantize_grouped_fused, fos_qdq_fused) need; the most groups the fused
@@ -139,6 +139,19 @@ typedef struct fos_tensor_desc {
 int fos_abi_version(void);
 const char* fos_status_string(int status);
 const char* fos_last_error(void);
+
+/* The fused calls' grid barrier waits a bounded number of polls (each at
+ * least 128 GPU cycles of sleep) before a workgroup gives up, sets
+ * FOS_STATUS_BARRIER_TIMEOUT and leaves its part of the outputs unwritten.
+ * The default, 2^20 polls, is about a second. This sets the limit for fused
+ * calls enqueued from now on, process-wide, and returns the previous one
+ * (-1 and no change for a negative value). A limit of 0 makes every
+ * workgroup that is not the barrier's last arrival give up at once, which
+ * lets a caller exercise its timeout handling (added in ABI version 5).
+ * A workgroup that gives up has still arrived at the barrier, so the
+ * barrier completes when the rest of the grid arrives: the workspace is
+ * left consistent and the next call on it is correct. */
+int fos_set_barrier_poll_limit(int polls);
 
 /* Global amax: NaN-dropping max |x| with start value +0, per tensor
  * (out[1]), per row (out[M]) or per 16-row band (out[M], M % 16 == 0).
@@ -236,14 +249,17 @@ int fos_quantize_columnwise(const void* x, int dtype, int64_t M, int64_t K, cons
  *              calls made one after another; calls that may run at the same time (different
  *              streams) need workspaces of their own.
  *   d_status:  nullable device int32; FOS_STATUS_BARRIER_TIMEOUT is set if
- *              the launch's grid-wide barrier does not complete within a
- *              bounded number of polls (about a second), in which case the
- *              codes and scales are incomplete. That happens only with a
- *              workspace that was not zero, or when other long-running work
- *              keeps part of the launch from becoming resident (the launch
- *              holds exactly as many workgroups as fit on the device; two
- *              fused calls on different streams can starve each other).
- *              Callers that may overlap fused calls should pass d_status. */
+ *              the launch's grid-wide barrier does not complete within the
+ *              poll limit (fos_set_barrier_poll_limit; about a second by
+ *              default), in which case the codes and scales are incomplete.
+ *              That happens only with a workspace that was not zero, or when
+ *              other long-running work keeps part of the launch from
+ *              becoming resident: the launch holds exactly as many
+ *              workgroups as fit on the device at once, so it needs the
+ *              whole device to itself (co-residency), and two fused calls
+ *              running at the same time on different streams can starve
+ *              each other. Pass d_status and check it to detect this; the
+ *              Python binding always passes one. */
 int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, uint8_t* codes,
                        uint8_t* scales, float* amax_out, float* sdec_out, void* workspace, int32_t* d_status,
                        void* stream);
@@ -284,8 +300,9 @@ int fos_qdq_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_conf
  *   d_status:       nullable device int32: FOS_STATUS_BAD_OFFS as for
  *                   fos_quantize_grouped, FOS_STATUS_BARRIER_TIMEOUT as for
  *                   fos_quantize_fused.
- * After FOS_STATUS_BARRIER_TIMEOUT from either fused call, clear the
- * workspace to zero again before its next use. */
+ * A workspace stays consistent after FOS_STATUS_BARRIER_TIMEOUT: the
+ * barrier's last arrival resets its counters and moves the grouped call
+ * counter on whether or not other workgroups gave up waiting. */
 int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
                                const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
                                float* group_sdec_out, void* workspace, int32_t* d_status, void* stream);

@@ -58,6 +58,7 @@ _SIGS = {
     "fos_abi_version": (_I, []),
     "fos_status_string": (ctypes.c_char_p, [_I]),
     "fos_last_error": (ctypes.c_char_p, []),
+    "fos_set_barrier_poll_limit": (_I, [_I]),
     "fos_amax": (_I, [_P, _I, _I64, _I64, _I, _P, _P]),
     "fos_quantize": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_qdq": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P]),
@@ -152,24 +153,92 @@ def fos_quantize(x: torch.Tensor, amax: torch.Tensor, *, codes=None, scales=None
     return codes, scales, sdec
 
 
-_workspaces: dict = {}
+def set_barrier_poll_limit(polls: int) -> int:
+    """Polls a fused call's grid barrier makes before giving up (process-wide,
+    for calls enqueued from now on); returns the previous limit."""
+    prev = load_library().fos_set_barrier_poll_limit(int(polls))
+    if prev < 0:
+        raise ValueError(f"poll limit must be >= 0, got {polls}")
+    return prev
 
 
-def fused_workspace(device) -> torch.Tensor:
-    """The zero-initialised workspace the fused calls use on `device` when
-    the caller passes none (one per device; calls on one device's streams
-    that may overlap need workspaces of their own)."""
+def _dev(device) -> torch.device:
     dev = torch.device(device)
-    if dev not in _workspaces:
-        _workspaces[dev] = torch.zeros(FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
-    return _workspaces[dev]
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    return dev
+
+
+# Default workspaces and status words of the fused calls, one of each per
+# (device, stream): calls on one stream run one after another and may share
+# them; calls on different streams may overlap and must not.
+_workspaces: dict = {}
+_status_words: dict = {}
+
+
+def _stream_key(device, stream=None):
+    dev = _dev(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    return dev, int(s.cuda_stream)
+
+
+def fused_workspace(device, stream=None) -> torch.Tensor:
+    """The zero-initialised workspace the fused calls use on `device` and
+    `stream` (default: the device's current stream) when the caller passes
+    none."""
+    key = _stream_key(device, stream)
+    if key not in _workspaces:
+        _workspaces[key] = torch.zeros(FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device=key[0])
+    return _workspaces[key]
+
+
+def fused_status_word(device, stream=None) -> torch.Tensor:
+    """The device int32 status word the fused calls on `device` and `stream`
+    OR their FOS_STATUS_* bits into when the caller passes none. Bits stay
+    set until read with fused_status()."""
+    key = _stream_key(device, stream)
+    if key not in _status_words:
+        _status_words[key] = torch.zeros(1, dtype=torch.int32, device=key[0])
+    return _status_words[key]
+
+
+def fused_status(device=None, stream=None, clear: bool = True) -> int:
+    """Synchronize `stream` and return the status bits the fused calls on it
+    have set since the last read (clearing them unless clear=False)."""
+    dev = _dev(device if device is not None else "cuda")
+    word = fused_status_word(dev, stream)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    s.synchronize()
+    v = int(word.item())
+    if clear and v:
+        with torch.cuda.stream(s):
+            word.zero_()
+        s.synchronize()
+    return v
+
+
+def _fused_done(dev, status, own_status: bool, check: bool):
+    """After a fused call: with check, synchronize and raise on a barrier
+    timeout (the outputs are then incomplete)."""
+    if not check:
+        return
+    torch.cuda.current_stream(dev).synchronize()
+    v = int(status.item())
+    if own_status and v:
+        status.zero_()
+        torch.cuda.current_stream(dev).synchronize()
+    if v & STATUS_BARRIER_TIMEOUT:
+        raise FosError(-1, "fused call: the grid barrier timed out; outputs are incomplete "
+                           "(another long-running kernel held part of the device)")
 
 
 def fos_quantize_fused(x: torch.Tensor, *, codes=None, scales=None, amax=None, sdec=None, status=None,
-                       workspace=None, **knobs):
+                       workspace=None, check=False, **knobs):
     """Amax (per tensor, or per row with scale_gran="row") and quantize in
     one launch. Returns (codes, scales, amax float32[1 or M], sdec float32[1
-    or M])."""
+    or M]). Without `workspace` / `status` the current stream's own are used
+    (fused_workspace, fused_status_word); with check=True the call
+    synchronizes and raises FosError if the grid barrier timed out."""
     _need(x, "x")
     M, K = x.shape
     cfg = config(**knobs)
@@ -185,16 +254,21 @@ def fos_quantize_fused(x: torch.Tensor, *, codes=None, scales=None, amax=None, s
         sdec = torch.empty(n_amax, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = fused_workspace(dev)
+    own = status is None
+    if own:
+        status = fused_status_word(dev)
     with torch.cuda.device(dev):
         _check(load_library().fos_quantize_fused(_ptr(x), DTYPES[x.dtype], M, K, ctypes.byref(cfg), _ptr(codes),
                                                  _ptr(scales), _ptr(amax), _ptr(sdec), _ptr(workspace),
                                                  _ptr(status), _stream(dev)))
+    _fused_done(dev, status, own, check)
     return codes, scales, amax, sdec
 
 
-def fos_qdq_fused(x: torch.Tensor, *, out=None, amax=None, status=None, workspace=None, **knobs):
+def fos_qdq_fused(x: torch.Tensor, *, out=None, amax=None, status=None, workspace=None, check=False, **knobs):
     """Per-tensor amax and fused quantize-dequantize in one launch (two when
-    the tensor does not fit on chip). Returns (y, amax float32[1])."""
+    the tensor does not fit on chip). Returns (y, amax float32[1]).
+    `workspace`, `status` and `check` as for fos_quantize_fused."""
     _need(x, "x")
     M, K = x.shape
     cfg = config(**knobs)
@@ -204,9 +278,13 @@ def fos_qdq_fused(x: torch.Tensor, *, out=None, amax=None, status=None, workspac
         amax = torch.empty(1, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = fused_workspace(dev)
+    own = status is None
+    if own:
+        status = fused_status_word(dev)
     with torch.cuda.device(dev):
         _check(load_library().fos_qdq_fused(_ptr(x), DTYPES[x.dtype], M, K, ctypes.byref(cfg), _ptr(y), _ptr(amax),
                                             _ptr(workspace), _ptr(status), _stream(dev)))
+    _fused_done(dev, status, own, check)
     return y, amax
 
 
@@ -298,9 +376,10 @@ def fos_quantize_grouped(x: torch.Tensor, offs: torch.Tensor, group_amax: torch.
 
 
 def fos_quantize_grouped_fused(x: torch.Tensor, offs: torch.Tensor, *, codes=None, scales=None, group_amax=None,
-                               group_sdec=None, status=None, workspace=None, **knobs):
+                               group_sdec=None, status=None, workspace=None, check=False, **knobs):
     """Group amaxes and the grouped quantize in one launch. Returns (codes,
-    scales, group_amax float32[G], group_sdec float32[G])."""
+    scales, group_amax float32[G], group_sdec float32[G]). `workspace`,
+    `status` and `check` as for fos_quantize_fused."""
     _need(x, "x")
     M, K = x.shape
     dev = x.device
@@ -316,9 +395,13 @@ def fos_quantize_grouped_fused(x: torch.Tensor, offs: torch.Tensor, *, codes=Non
         group_sdec = torch.empty(G, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = fused_workspace(dev)
+    own = status is None
+    if own:
+        status = fused_status_word(dev)
     with torch.cuda.device(dev):
         _check(load_library().fos_quantize_grouped_fused(_ptr(x), DTYPES[x.dtype], M, K, _ptr(offs), G,
                                                          ctypes.byref(cfg), _ptr(codes), _ptr(scales),
                                                          _ptr(group_amax), _ptr(group_sdec), _ptr(workspace),
                                                          _ptr(status), _stream(dev)))
+    _fused_done(dev, status, own, check)
     return codes, scales, group_amax, group_sdec

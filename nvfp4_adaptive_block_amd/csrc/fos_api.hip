@@ -3,6 +3,7 @@
 // or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -16,6 +17,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Polls a fused call's grid barrier makes before giving up (process-wide).
+std::atomic<int> g_poll_limit{fos::kDefaultSpinLimit};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -135,6 +139,11 @@ const char* fos_status_string(int status) {
 }
 
 const char* fos_last_error(void) { return g_last_error.c_str(); }
+
+int fos_set_barrier_poll_limit(int polls) {
+  if (polls < 0) return -1;
+  return g_poll_limit.exchange(polls, std::memory_order_relaxed);
+}
 
 int fos_amax(const void* x, int dtype, int64_t M, int64_t K, int gran, float* amax_out, void* stream) {
   int rc;
@@ -380,6 +389,7 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   a.scales = scales;
   a.sdec_out = sdec_out;
   a.status = d_status;
+  a.spin_limit = g_poll_limit.load(std::memory_order_relaxed);
   if (cfg->scale_gran == FOS_PER_ROW) {  // per-row segments, one wave per row at a time
     a.total_units = M * ((a.t[0].K / 16 + ub - 1) / ub);
     return launch_status(fos::launch_fused_row(dtype, cfg->recipe, metric, prec, order, a, amax_out,
@@ -416,6 +426,7 @@ int fos_qdq_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_conf
   a.total_units = (M * (K / 16) + ub - 1) / ub;
   a.six_b = six_b(cfg);
   a.status = d_status;
+  a.spin_limit = g_poll_limit.load(std::memory_order_relaxed);
   bool done = false;
   if ((rc = launch_status(fos::launch_fused_qdq(dtype, cfg->recipe, metric, prec, order, a,
                                                 static_cast<uint32_t*>(workspace), amax_out, &done, s))))
@@ -458,6 +469,7 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
   a.scales = scales;
   a.sdec_out = group_sdec_out;
   a.status = d_status;
+  a.spin_limit = g_poll_limit.load(std::memory_order_relaxed);
   a.offs = offs;
   return launch_status(fos::launch_fused_grouped(dtype, cfg->recipe, metric, prec, order, a,
                                                  static_cast<uint32_t*>(workspace), group_amax_out,

@@ -18,6 +18,10 @@ enum { kOutQuant = 0, kOutQdq = 1 };
 enum { kAmaxTensor = 0, kAmaxRow = 1, kAmaxBand16 = 2 };
 enum { kStatusTileNonuniform = 1, kStatusBadOffs = 2, kStatusBarrier = 4 };
 
+// Polls of the fused kernels' grid barrier before a workgroup gives up
+// (each poll sleeps at least 128 cycles first): about a second.
+constexpr int kDefaultSpinLimit = 1 << 20;
+
 // Bytes of the fused kernels' workspace (the grid barrier's counters and
 // the grouped kernel's per-group maxima), and the most groups the fused
 // grouped kernel takes.
@@ -70,6 +74,7 @@ struct Args1x16 {
   int32_t* status;  // nullable device status word
   const int32_t* offs;       // grouped: cumulative end offsets [G]
   const float* group_amax;   // grouped: [G]
+  int spin_limit;            // fused calls: polls before the grid barrier gives up
 };
 
 struct Args16x16 {

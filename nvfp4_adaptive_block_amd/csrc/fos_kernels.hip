@@ -1277,8 +1277,8 @@ __global__ void k_band16(float* out, int64_t nbands) {
 // The grid holds only as many workgroups as fit on the device at once, so
 // they all become resident unless other long-running work holds CUs (for
 // example a second fused launch on another stream). The poll is bounded
-// either way: after kSpinLimit polls a workgroup sets kStatusBarrier and
-// returns without quantizing rather than wait forever.
+// either way: after args.spin_limit polls a workgroup sets kStatusBarrier
+// and returns without quantizing rather than wait forever.
 
 // max |x| bits over blocks [b0, b1) of a flattened tensor: lane l takes
 // blocks b0 + l + 64 k, four in flight.
@@ -1315,8 +1315,7 @@ __device__ __forceinline__ uint32_t range_absmax(const void* x, int64_t b0, int6
   else return pair_key_to_f32_bits<DT>(k);
 }
 
-constexpr int kBarGroups = 32;       // first-level arrival groups
-constexpr int kSpinLimit = 1 << 20;  // polls before giving up (each at least 128 cycles of sleep)
+constexpr int kBarGroups = 32;  // first-level arrival groups
 
 // Word offsets in the workspace; every counter and maximum sits on a
 // 128-byte line of its own. The published word (8-byte aligned) holds the
@@ -1342,7 +1341,13 @@ static_assert((BarWs::kSlotBase + 4 * kMaxFusedGroups) * 4 <= kFusedWorkspaceByt
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Called by one thread per workgroup with the workgroup's max; returns false
-// when the poll limit was reached.
+// when `spin_limit` polls passed without the barrier completing. The last
+// arrival (which runs exactly once per barrier, after every workgroup has
+// arrived) also adds 1 to *bump when bump is not null, before publishing.
+//
+// A workgroup that gives up has still arrived, so the barrier completes once
+// the rest of the grid arrives: its counters end at zero and *bump is bumped
+// whether or not any workgroup waited for it.
 //
 // Every value that crosses workgroups travels through an atomic read-modify-
 // write or an agent-scope atomic load or store (which the compiler issues
@@ -1362,7 +1367,8 @@ __device__ __forceinline__ uint32_t barrier_generation(const BarWs& ws) {
   return (uint32_t)p;
 }
 
-__device__ bool grid_max_barrier(const BarWs& ws, uint32_t g0, uint32_t m, uint32_t& result) {
+__device__ bool grid_max_barrier(const BarWs& ws, uint32_t g0, uint32_t m, uint32_t& result, uint32_t* bump,
+                                 int spin_limit) {
   constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
   constexpr int kR = __ATOMIC_RELAXED;
   const uint32_t G = gridDim.x;
@@ -1380,12 +1386,16 @@ __device__ bool grid_max_barrier(const BarWs& ws, uint32_t g0, uint32_t m, uint3
     if (__hip_atomic_fetch_add(ws.tcount(), 1u, kR, kA) == ng - 1) {
       const uint32_t a = __hip_atomic_exchange(ws.tmax(), 0u, kR, kA);
       __hip_atomic_store(ws.tcount(), 0u, kR, kA);
+      if (bump) {
+        __hip_atomic_fetch_add(bump, 1u, kR, kA);
+        vm_wait();
+      }
       __hip_atomic_store(ws.pub(), ((uint64_t)a << 32) | (uint64_t)(g0 + 1u), kR, kA);
     }
   }
   uint64_t p = __hip_atomic_load(ws.pub(), kR, kA);
   for (int it = 0; (uint32_t)p == g0; it++) {
-    if (it >= kSpinLimit) return false;
+    if (it >= spin_limit) return false;
     __builtin_amdgcn_s_sleep(2);
     p = __hip_atomic_load(ws.pub(), kR, kA);
   }
@@ -1420,7 +1430,8 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
     uint32_t a = 0;
     const BarWs ws{workspace};
     const uint32_t g0 = barrier_generation(ws);
-    ok = grid_max_barrier(ws, g0, max(max(part[0], part[1]), max(part[2], part[3])), a) ? 1 : 0;
+    ok = grid_max_barrier(ws, g0, max(max(part[0], part[1]), max(part[2], part[3])), a, nullptr,
+                          args.spin_limit) ? 1 : 0;
     amax_bits = a;
     if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
   }
@@ -1568,7 +1579,8 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
     uint32_t a = 0;
     const BarWs ws{workspace};
     const uint32_t g0 = barrier_generation(ws);
-    ok = grid_max_barrier(ws, g0, max(max(part[0], part[1]), max(part[2], part[3])), a) ? 1 : 0;
+    ok = grid_max_barrier(ws, g0, max(max(part[0], part[1]), max(part[2], part[3])), a, nullptr,
+                          args.spin_limit) ? 1 : 0;
     amax_bits = a;
     if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
   }
@@ -1716,7 +1728,9 @@ __global__ void __launch_bounds__(256) k_fused_row(const Args1x16<1> args, float
 // Slots are banked: a grouped call accumulates in bank ggen % 2 (ggen counts
 // grouped calls and is read before arriving, so every workgroup sees the
 // same value), and workgroup 0 clears all of the other bank, which the next
-// grouped call uses, and bumps ggen once the barrier has passed.
+// grouped call uses. The barrier's last arrival bumps ggen, so the next call
+// moves to the cleared bank even when some workgroups (workgroup 0
+// included) gave up waiting.
 template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
 __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, uint32_t* workspace, float* amax_out) {
   constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
@@ -1793,7 +1807,7 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t unused = 0;
-    ok = grid_max_barrier(ws, gen0, 0u, unused) ? 1 : 0;
+    ok = grid_max_barrier(ws, gen0, 0u, unused, ws.ggen(), args.spin_limit) ? 1 : 0;
     if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
   }
   __syncthreads();
@@ -1801,7 +1815,6 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
   for (int g = threadIdx.x; g < G; g += blockDim.x) gm[g] = __hip_atomic_load(ws.gslot(bank, g), kR, kA);
   __syncthreads();
   if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ws.ggen(), 1u, kR, kA);
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
       const float A = __uint_as_float(gm[g]);
       if (amax_out) amax_out[g] = A;

@@ -31,13 +31,18 @@ def test_library_exports_every_declared_symbol():
 
 def test_host_only_calls():
     lib = fos.load_library()
-    assert lib.fos_abi_version() == 4
+    assert lib.fos_abi_version() == 5
     assert lib.fos_status_string(0) == b"ok"
     assert lib.fos_status_string(3) == b"unsupported shape"
     # a shape error is reported before any device is touched
     cfg = fos.config()
     rc = lib.fos_quantize(None, 0, 4, 40, None, ctypes.byref(cfg), None, None, None, None, None)
     assert rc != 0
+    # the barrier's poll limit: set, read back through the previous value, restored
+    prev = lib.fos_set_barrier_poll_limit(7)
+    assert prev == 1 << 20
+    assert lib.fos_set_barrier_poll_limit(-1) == -1
+    assert lib.fos_set_barrier_poll_limit(prev) == 7
 
 
 def test_fused_calls_validate_before_touching_a_device():
