@@ -215,6 +215,67 @@ def test_qdq_is_dequantize_of_quantize(orc, dtype, recipe, metric, prec, bound):
     np.testing.assert_array_equal(y, want)
 
 
+def _round_to(xh: np.ndarray, dtype: str) -> np.ndarray:
+    """Raw bits of float32 values rounded to dtype (RNE, overflow to inf) by
+    numpy (fp16) or torch (bf16), independently of the oracle's rounding."""
+    if dtype == "fp32":
+        return xh.astype(np.float32)
+    if dtype == "fp16":
+        with np.errstate(over="ignore"):
+            return xh.astype(np.float16).view(np.uint16)
+    return raw_bits(torch.from_numpy(xh).to(torch.bfloat16))
+
+
+def _cmp_bits(a, b, msg=""):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    if a.dtype == np.float32:
+        a, b = a.view(np.uint32), b.view(np.uint32)
+    np.testing.assert_array_equal(a, b, err_msg=msg)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("gran", ["tensor", "row"])
+def test_dequantize_matches_independent_decode(orc, out_dtype, gran):
+    """nvfp4_dequantize (pytorch/ao PR, recipe commit: the recipe-agnostic
+    decode, with row-scaled global scales) on random codes covering all 16
+    nibbles, random finite block scales and S_dec that differs from row to
+    row (a wide range: fp16 outputs overflow to inf, some underflow), equals
+    the numpy decode RN(val(q) * RN(sigma * S_dec)) rounded to the output
+    type by numpy or torch."""
+    M, K = 48, 160
+    codes = synthdata.random_packed_codes(M, K, 91)
+    scales = synthdata.random_block_scales(M, K, 92)
+    rng = np.random.default_rng(93)
+    n = M if gran == "row" else 1
+    sdec = (2.0 ** rng.uniform(-30, 12, n)).astype(np.float32)
+    if gran == "row":
+        sdec[:4] = [1.0, 2.0 ** -140, 3.0e-3, 7.5]  # includes a subnormal S_dec
+    y = orc.dequantize(codes, scales, sdec, gran, out_dtype)
+    _cmp_bits(y, _round_to(decode(codes, scales, sdec, gran), out_dtype), f"{out_dtype} {gran}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("block,gran", [("1x16", "tensor"), ("1x16", "row"), ("16x16", "tensor"), ("16x16", "row")])
+def test_qdq_every_dtype_block_and_granularity(orc, dtype, block, gran):
+    """The fused QDQ output is the kept candidate's decoded values rounded
+    once to the input type, for every input type, block shape and scale
+    granularity the quantizer takes: it equals the numpy decode of the
+    quantizer's own codes, scales and S_dec, rounded by numpy or torch. The
+    16x16 per-row amax is uniform within each band (the tile-uniform
+    contract), and the per-row S_dec differs from band to band."""
+    M, K = 64, 192
+    t = _x("outlier", dtype, M, K, 111)
+    bits = raw_bits(t)
+    mode = "tensor" if gran == "tensor" else ("band16" if block == "16x16" else "row")
+    amax = orc.amax(bits, dtype, mode)
+    for (recipe, metric, prec), bound in [(("nvfp4", "mse", "exact"), 448), (("4over6", "mse", "exact"), 448),
+                                          (("4over6", "mae", "fp16"), 256)]:
+        kw = dict(recipe=recipe, block=block, scale_gran=gran, err_metric=metric, err_prec=prec, bound=bound)
+        q = orc.quantize(bits, dtype, amax, **kw)
+        y = orc.qdq(bits, dtype, amax, **kw)
+        _cmp_bits(y, _round_to(decode(q["codes"], q["scales"], q["sdec"], gran), dtype), f"{dtype} {kw}")
+
+
 def test_grouped_equals_per_group(orc):
     M, pad, K, G = 512, 48, 128, 12
     x, offs, fac = synthdata.grouped_tokens(M, pad, K, G, seeds=(1, 2, 3, 4))

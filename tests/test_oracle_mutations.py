@@ -53,6 +53,12 @@ MUTATIONS = [
     ("per-row amax indexed by tensor", r"\? amax\[0\] : amax\[r0\];", "? amax[0] : amax[0];"),
     ("grouped padding not cleared", r"memset\(codes \+ M \* \(K / 2\), 0,", "memset(codes + M * (K / 2), 1,"),
     ("binary16 rounding truncates", r"return nearbyint\(a / q\) \* q;", "return trunc(a / q) * q;"),
+    ("per-row dequantize reads the first S_dec", r"\? sdec\[0\] : sdec\[r\];", "? sdec[0] : sdec[0];"),
+    ("16x16 decoded values all go to the tile's first row",
+     r"xhat_out\[r \* K \+ cb \* 16 \+ j\] = xhat\[16 \* i \+ j\]",
+     "xhat_out[r0 * K + cb * 16 + j] = xhat[16 * i + j]"),
+    ("fp32 outputs rounded through bf16", r"\(\(float\*\)y\)\[idx\] = v;",
+     "((float*)y)[idx] = oracle_bf16_bits_to_f32(oracle_f32_to_bf16_rne(v));"),
 ]
 
 
@@ -86,6 +92,10 @@ def _battery(orc):
     inv.test_amax_modes(orc, "bf16")
     inv.test_qdq_is_dequantize_of_quantize(orc, "bf16", "4over6", "mse", "fp16", 448)
     inv.test_grouped_equals_per_group(orc)
+    for out_dtype, gran in (("fp32", "row"), ("bf16", "tensor")):
+        inv.test_dequantize_matches_independent_decode(orc, out_dtype, gran)
+    for dtype, block, gran in (("fp32", "1x16", "tensor"), ("bf16", "16x16", "row"), ("fp16", "1x16", "row")):
+        inv.test_qdq_every_dtype_block_and_granularity(orc, dtype, block, gran)
 
 
 def _build(tmp_path, source, name):
