@@ -307,6 +307,27 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
                                const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
                                float* group_sdec_out, void* workspace, int32_t* d_status, void* stream);
 
+/* fos_quantize_grouped_fused without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The call allocates
+ * nothing; the caller still passes every input and output.
+ * The workspace is a library-held device array of FOS_FUSED_WORKSPACE_BYTES
+ * (16 KiB), one copy per device, held until the process ends. Its address
+ * is looked up on the first call on each device (that call, unless its
+ * stream is being captured, also clears the array with a fill kernel on
+ * `stream`). It holds the grid barrier's counters and the per-group maxima
+ * of at most FOS_FUSED_MAX_GROUPS groups: G beyond that returns
+ * FOS_ERR_INVALID_ARG and enqueues nothing. Every call on a device shares
+ * that device's array and leaves it ready for the next call, so calls that
+ * may overlap on one device (different streams) race and must not be made;
+ * calls on one stream, or synchronized with each other, are safe.
+ * Arguments, results and errors are otherwise those of
+ * fos_quantize_grouped_fused (added in ABI version 5). */
+int fos_quantize_grouped_fused_noalloc(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs,
+                                       int G, const fos_config* cfg, uint8_t* codes, uint8_t* scales,
+                                       float* group_amax_out, float* group_sdec_out, int32_t* d_status,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

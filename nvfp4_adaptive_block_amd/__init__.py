@@ -70,6 +70,8 @@ _SIGS = {
     "fos_quantize_columnwise": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P]),
     "fos_quantize_grouped_fused": (_I, [_P, _I, _I64, _I64, _P, _I, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P,
                                         _P]),
+    "fos_quantize_grouped_fused_noalloc": (_I, [_P, _I, _I64, _I64, _P, _I, ctypes.POINTER(_Config), _P, _P, _P, _P,
+                                                _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -404,4 +406,21 @@ def fos_quantize_grouped_fused(x: torch.Tensor, offs: torch.Tensor, *, codes=Non
                                                          _ptr(group_amax), _ptr(group_sdec), _ptr(workspace),
                                                          _ptr(status), _stream(dev)))
     _fused_done(dev, status, own, check)
+    return codes, scales, group_amax, group_sdec
+
+
+def fos_quantize_grouped_fused_noalloc(x: torch.Tensor, offs: torch.Tensor, *, codes, scales, group_amax,
+                                       group_sdec=None, status=None, **knobs):
+    """fos_quantize_grouped_fused with the library-held workspace (the C call
+    allocates nothing). The caller passes every output buffer. Calls on
+    different streams of one device must not overlap."""
+    _need(x, "x")
+    M, K = x.shape
+    dev = x.device
+    cfg = config(**knobs)
+    with torch.cuda.device(dev):
+        _check(load_library().fos_quantize_grouped_fused_noalloc(_ptr(x), DTYPES[x.dtype], M, K, _ptr(offs),
+                                                                 offs.numel(), ctypes.byref(cfg), _ptr(codes),
+                                                                 _ptr(scales), _ptr(group_amax), _ptr(group_sdec),
+                                                                 _ptr(status), _stream(dev)))
     return codes, scales, group_amax, group_sdec

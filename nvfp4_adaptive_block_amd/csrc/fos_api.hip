@@ -117,6 +117,53 @@ void mode_of(const fos_config* c, int& metric, int& prec, int& order) {
 
 }  // namespace
 
+// The workspace of fos_quantize_grouped_fused_noalloc, held by the library:
+// one copy per device (each GPU keeps its own until the process ends), zero
+// when the code object loads. Host code never passes this name to a kernel:
+// in host code it is a stand-in, not a device address. The device address of
+// each GPU's copy comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[FOS_FUSED_WORKSPACE_BYTES];
+
+namespace {
+
+int check_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                        const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
+                        float* group_sdec_out, int32_t* d_status);
+int launch_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                         const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
+                         float* group_sdec_out, void* workspace, int32_t* d_status, void* stream);
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current. The first call on a device that is not under stream
+// capture also clears it with a fill kernel on `s` (ordered before the call's
+// own launch); under capture the load-time zeros stand, since no call has
+// used this device's copy yet.
+int scratch_address(hipStream_t s, void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(FOS_ERR_DEVICE, "no current HIP device (or ordinal %d >= 64)", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FOS_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
+    if (cs == hipStreamCaptureStatusNone) {
+      const hipError_t z = fos::launch_zero_u32(p, FOS_FUSED_WORKSPACE_BYTES / 4, s);
+      if (z != hipSuccess) return fail(FOS_ERR_LAUNCH, "clearing the scratch failed: %s", hipGetErrorString(z));
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return FOS_OK;
+}
+
+}  // namespace
+
 static_assert(FOS_FUSED_WORKSPACE_BYTES == fos::kFusedWorkspaceBytes, "workspace size mismatch");
 static_assert(FOS_FUSED_MAX_GROUPS == fos::kMaxFusedGroups, "group limit mismatch");
 
@@ -441,6 +488,43 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
                                const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
                                float* group_sdec_out, void* workspace, int32_t* d_status, void* stream) {
   int rc;
+  if ((rc = check_grouped_fused(x, dtype, M_alloc, K, offs, G, cfg, codes, scales, group_amax_out, group_sdec_out,
+                                d_status)))
+    return rc;
+  if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (!aligned(workspace, 8)) return fail(FOS_ERR_ALIGN, "workspace misaligned");
+  if ((rc = check_device())) return rc;
+  return launch_grouped_fused(x, dtype, M_alloc, K, offs, G, cfg, codes, scales, group_amax_out, group_sdec_out,
+                              workspace, d_status, stream);
+}
+
+int fos_quantize_grouped_fused_noalloc(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs,
+                                       int G, const fos_config* cfg, uint8_t* codes, uint8_t* scales,
+                                       float* group_amax_out, float* group_sdec_out, int32_t* d_status,
+                                       void* stream) {
+  if (G > FOS_FUSED_MAX_GROUPS)
+    return fail(FOS_ERR_INVALID_ARG, "G=%d exceeds the %d groups the library-held scratch holds", G,
+                FOS_FUSED_MAX_GROUPS);
+  // argument checks first, so that a rejected call touches no device state
+  int rc;
+  if ((rc = check_grouped_fused(x, dtype, M_alloc, K, offs, G, cfg, codes, scales, group_amax_out, group_sdec_out,
+                                d_status)))
+    return rc;
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(static_cast<hipStream_t>(stream), &ws))) return rc;
+  return launch_grouped_fused(x, dtype, M_alloc, K, offs, G, cfg, codes, scales, group_amax_out, group_sdec_out, ws,
+                              d_status, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                        const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
+                        float* group_sdec_out, int32_t* d_status) {
+  int rc;
   if ((rc = check_dtype(dtype))) return rc;
   if ((rc = check_cfg(cfg))) return rc;
   if (cfg->block != FOS_BLOCK_1X16) return fail(FOS_ERR_CONFIG, "grouped quantize supports 1x16 blocks");
@@ -448,13 +532,16 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
   if (G <= 0 || G > FOS_FUSED_MAX_GROUPS)
     return fail(FOS_ERR_INVALID_ARG, "G must be in [1, %d], got %d", FOS_FUSED_MAX_GROUPS, G);
   if (!offs) return fail(FOS_ERR_INVALID_ARG, "offs must be non-NULL");
-  if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
   if (M_alloc * K > 0 && (!x || !codes || !scales)) return fail(FOS_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
   if (!aligned(x, 16) || !aligned(codes, 8)) return fail(FOS_ERR_ALIGN, "x or codes misaligned");
-  if (!aligned(offs, 4) || !aligned(group_amax_out, 4) || !aligned(group_sdec_out, 4) || !aligned(d_status, 4) ||
-      !aligned(workspace, 8))
-    return fail(FOS_ERR_ALIGN, "offs/amax/sdec/status/workspace misaligned");
-  if ((rc = check_device())) return rc;
+  if (!aligned(offs, 4) || !aligned(group_amax_out, 4) || !aligned(group_sdec_out, 4) || !aligned(d_status, 4))
+    return fail(FOS_ERR_ALIGN, "offs/amax/sdec/status misaligned");
+  return FOS_OK;
+}
+
+int launch_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_t K, const int32_t* offs, int G,
+                         const fos_config* cfg, uint8_t* codes, uint8_t* scales, float* group_amax_out,
+                         float* group_sdec_out, void* workspace, int32_t* d_status, void* stream) {
   int metric, prec, order;
   mode_of(cfg, metric, prec, order);
   fos::Args1x16<1> a;
@@ -476,4 +563,4 @@ int fos_quantize_grouped_fused(const void* x, int dtype, int64_t M_alloc, int64_
                                                  static_cast<hipStream_t>(stream)));
 }
 
-}  // extern "C"
+}  // namespace
