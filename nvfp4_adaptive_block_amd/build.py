@@ -33,14 +33,17 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(out: str = LIB, extra: list[str] | None = None, quiet: bool = True) -> str:
+def build(out: str = LIB, extra: list[str] | None = None, quiet: bool = True, sources: list[str] | None = None) -> str:
+    """Compile `sources` (default: the library) into the shared object `out`
+    with the library's flags and include paths. Other sources built this way
+    (test kernels that call the device helpers) get the same numerics."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, *(sources or SOURCES), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed building libfos.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     if msgs and not quiet:
         sys.stderr.write("\n".join(msgs) + "\n")
     os.replace(tmp, out)

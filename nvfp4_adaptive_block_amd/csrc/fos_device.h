@@ -3,12 +3,13 @@
 //
 // Every function here computes one step of the quantizer bit-exactly: one
 // binary32 operation per step, round to nearest even. Conversions use
-// gfx950's convert instructions where those were checked exhaustively against
-// the format definitions (every binary32 input), and plain integer/float code
-// elsewhere:
+// gfx950's convert instructions where those are checked exhaustively against
+// the format definitions (tests/test_gpu_primitives.py runs these helpers on
+// the device over every input the kernels can feed them and compares each
+// result bitwise with the CPU), and plain integer/float code elsewhere:
 //   - f32 -> E2M1 pair (v_cvt_scalef32_pk_fp4_f32, scale 1.0): RNE with
 //     saturation to +-6 for every non-NaN input, -0 kept; a NaN becomes
-//     (sign | 6), so blocks holding a NaN take the careful path, which encodes
+//     (sign | 7), i.e. +-6, so blocks holding a NaN take the careful path, which encodes
 //     NaN as +6 (the NaN rule the kernel page, wolfcomos/ao PR "Add a CuTe DSL
 //     fast-path kernel for four-over-six quantize", states).
 //   - E2M1 pair -> f32 (v_cvt_scalef32_pk_f32_fp4, scale 1.0): exact.
@@ -48,12 +49,6 @@ __device__ __forceinline__ float f16_lo(uint32_t w) {
 }
 __device__ __forceinline__ float f16_hi(uint32_t w) {
   _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-  return (float)h;
-}
-
-// binary32 -> binary16 -> binary32 (RNE, overflow to inf)
-__device__ __forceinline__ float round_f16(float v) {
-  _Float16 h = (_Float16)opaque(v);
   return (float)h;
 }
 
@@ -117,16 +112,20 @@ __device__ __forceinline__ void e2m1_unpack8(uint32_t w, float* out) {
 
 // ---------------------------------------------------------------- division
 
-// RN(a / 6) for a >= 0 (or NaN): a product with RN(1/6) corrected by one
-// fused multiply-add of the exact remainder. Checked exhaustively on every
-// non-negative binary32 input: it is correctly rounded except where the
-// quotient is subnormal (a < 2^-125), which takes the division instead.
+// RN(a / 6) for a >= 0 (a NaN gives a NaN): a product with RN(1/6)
+// corrected by one fused multiply-add of the exact remainder. That formula is
+// correctly rounded for every finite a >= 2^-125 (tests/test_div6_formula.py
+// runs it on every binary32 on the CPU). Below, some quotients are subnormal
+// and it is not; at +inf the remainder is inf - inf. Those inputs take the
+// division instead, so the helper is RN(a / 6) on every a from +0 to +inf
+// (tests/test_gpu_primitives.py runs it on each of them on the device).
 __device__ __forceinline__ float div6(float a) {
   constexpr float r6 = 0x1.555556p-3f;  // RN(1/6)
   const float q0 = a * r6;
   const float r = __builtin_fmaf(-q0, 6.0f, a);
   float q = __builtin_fmaf(r, r6, q0);
-  if (__ballot(a < 0x1p-125f)) q = (a < 0x1p-125f) ? a / 6.0f : q;
+  const bool slow = (a < 0x1p-125f) || (a > kFltMax);
+  if (__ballot(slow)) q = slow ? a / 6.0f : q;
   return q;
 }
 

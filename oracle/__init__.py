@@ -74,6 +74,7 @@ _SIGS = {
     "oracle_f32_to_bf16_rne_array": (None, [_P, _I64, _P]),
     "oracle_global_encode_scale": (ctypes.c_float, [ctypes.c_float, ctypes.c_int]),
     "oracle_global_decode_scale": (ctypes.c_float, [ctypes.c_float, ctypes.c_int]),
+    "oracle_global_scales_array": (None, [_P, _I64, ctypes.c_int, _P, _P]),
     "oracle_tree16": (ctypes.c_float, [_P]),
     "oracle_seq16": (ctypes.c_float, [_P]),
     "oracle_amax": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_int, _P]),
@@ -167,6 +168,14 @@ class Oracle:
 
     def global_decode_scale(self, amax: float, bound: int) -> float:
         return self.lib.oracle_global_decode_scale(amax, bound)
+
+    def global_scales(self, amax, bound: int):
+        """(S_enc, S_dec) arrays of an array of amaxes."""
+        a = np.ascontiguousarray(amax, dtype=np.float32)
+        enc = np.empty(a.shape, np.float32)
+        dec = np.empty(a.shape, np.float32)
+        self.lib.oracle_global_scales_array(_ptr(a), a.size, bound, _ptr(enc), _ptr(dec))
+        return enc, dec
 
     def seq16(self, u) -> float:
         u = np.ascontiguousarray(u, dtype=np.float32)

@@ -225,6 +225,15 @@ float oracle_global_decode_scale(float A, int bound) {
     return 1.0f / oracle_global_encode_scale(A, bound);
 }
 
+/* array forms of the two global scales (for exhaustive pins) */
+void oracle_global_scales_array(const float* amax, int64_t n, int e4m3_bound, float* s_enc, float* s_dec) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        s_enc[i] = oracle_global_encode_scale(amax[i], e4m3_bound);
+        s_dec[i] = oracle_global_decode_scale(amax[i], e4m3_bound);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Reductions                                                          */
 /* ------------------------------------------------------------------ */

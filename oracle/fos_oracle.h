@@ -83,6 +83,7 @@ void oracle_f32_to_bf16_rne_array(const float* x, int64_t n, uint16_t* out);
 /* global scales */
 float oracle_global_encode_scale(float amax, int e4m3_bound);
 float oracle_global_decode_scale(float amax, int e4m3_bound);
+void oracle_global_scales_array(const float* amax, int64_t n, int e4m3_bound, float* s_enc, float* s_dec);
 
 /* T16 reduction of 16 terms in the pinned order */
 float oracle_tree16(const float* u);
