@@ -2,7 +2,9 @@
 benchmark times: the whole tensor goes through the library in one call, and
 the oracle recomputes sampled rows (1x16; per-row independence given the
 global scale) or sampled 16-row bands (16x16). Global amaxes are compared in
-full. Every knob combination of each workload is run.
+full. Every knob combination of each workload is run; reused output buffers
+are filled with a sentinel byte before each call. One mode per workload is
+compared on the whole tensor in test_gpu_fullsize_whole.py.
 
 Workloads: the dense activation tensor (bf16 8192x4096, four data families),
 the 16x16 weights (bf16 4096x14336, fp32 4096x4096), the fused-QDQ expert
@@ -55,6 +57,8 @@ def test_dense_activation_8192x4096(orc, family):
     for (recipe, metric, prec), bound, gran in itertools.product(MODES, BOUNDS, ("tensor", "row")):
         kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, scale_gran=gran)
         a = am[gran]
+        codes.fill_(0xA5)  # sentinel: a block left unwritten shows
+        scales.fill_(0xA5)
         _, _, sdec = fos.fos_quantize(xd, torch.from_numpy(a).to("cuda"), codes=codes, scales=scales, **kw)
         torch.cuda.synchronize()
         want = orc.quantize(bits[rows], "bf16", a if gran == "tensor" else a[rows], **kw)
@@ -80,6 +84,8 @@ def test_weights_16x16(orc, dtype, M, K, seed):
     for (recipe, metric, prec), bound, gran in itertools.product(MODES, BOUNDS, ("tensor", "row")):
         kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, scale_gran=gran, block="16x16")
         a = am[gran]
+        codes.fill_(0xA5)  # sentinel: a block left unwritten shows
+        scales.fill_(0xA5)
         fos.fos_quantize(xd, torch.from_numpy(a).to("cuda"), codes=codes, scales=scales, status=status, **kw)
         torch.cuda.synchronize()
         want = orc.quantize(bits[rows], dtype, a if gran == "tensor" else a[rows], **kw)
@@ -130,6 +136,8 @@ def test_grouped_moe_65536x7168(orc):
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     for bound in BOUNDS:
         kw = dict(recipe="4over6", err_metric="mse", err_prec="exact", bound=bound)
+        codes.fill_(0xA5)  # sentinel: a block left unwritten shows
+        scales.fill_(0xA5)
         fos.fos_quantize_grouped(xd, torch.from_numpy(offs).to("cuda"), torch.from_numpy(gam).to("cuda"),
                                  codes=codes, scales=scales, group_sdec=gsdec, status=status, **kw)
         torch.cuda.synchronize()
