@@ -22,12 +22,12 @@
 // 127 E4M3 values, so for each global scale the wave keeps, in LDS, the
 // encode multipliers RN(S_enc / sigma) and decode multipliers
 // RN(sigma * S_dec) of all 127 codes, rebuilt when the wave's tensor (or
-// row) changes. A unit whose lanes straddle rows of different global scales
-// divides per lane instead.
+// row, or group) changes. Every unit has one global scale: per-row units
+// are segments of one row, and flat grouped units never cross a group.
 //
-// 16x16 tiles: a lane owns one 16-element row segment of a tile, the 16 lanes
-// of a DPP row hold the tile's rows, and the tile amax and error sums cross
-// lanes. A unit is one 16-row band times four tiles.
+// 16x16 tiles: four consecutive lanes own a tile (lane j of the four holds
+// the tile's rows j, j + 4, j + 8, j + 12), and the tile amax and error sums
+// cross those lanes. A unit is one 16-row band times 16 tiles.
 #include "fos_device.h"
 #include "fos_kernels.h"
 
@@ -217,28 +217,19 @@ struct Table {
 };
 
 // One candidate's block scale and multipliers: t = RN(q * S_enc) with q the
-// already divided block amax (RN(a/6) or RN(a/4)); scale = E4M3(t). With
-// TAB the multipliers come from the wave's table, otherwise they are
-// computed here with correctly rounded division.
+// already divided block amax (RN(a/6) or RN(a/4)); scale = E4M3(t); the
+// multipliers E = RN(S_enc / sigma) and D = RN(sigma * S_dec) come from the
+// wave's table.
 struct Cand {
   uint32_t scale;
   float E, D;
 };
 
-template <bool TAB>
-__device__ __forceinline__ Cand make_cand(float q, float S_enc, float S_dec, const Table& tab) {
+__device__ __forceinline__ Cand make_cand(float q, float S_enc, const Table& tab) {
   Cand c;
   c.scale = e4m3_code(q * S_enc);
-  if (TAB) {
-    c.E = tab.E[c.scale];
-    c.D = tab.D[c.scale];
-  } else {
-    const float sigma = e4m3_value(c.scale);
-    const bool zero = sigma == 0.0f;
-    const float e = S_enc / (zero ? 1.0f : sigma);
-    c.E = zero ? 0.0f : __builtin_fminf(e, kFltMax);
-    c.D = sigma * S_dec;
-  }
+  c.E = tab.E[c.scale];
+  c.D = tab.D[c.scale];
   return c;
 }
 
@@ -316,11 +307,11 @@ struct BlockOut {
 // Quantize one 1x16 block held in x. When NEED_XHAT, xh receives the kept
 // candidate's decoded values. Returns false when the fast form cannot be
 // trusted (the block holds a NaN); the caller then reruns with CAREFUL.
-template <int RECIPE, int METRIC, int PREC, int ORDER, bool CAREFUL, bool NEED_XHAT, bool TAB>
+template <int RECIPE, int METRIC, int PREC, int ORDER, bool CAREFUL, bool NEED_XHAT>
 __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_dec, const Table& tab, BlockOut& o,
                                            float* xh) {
   const float a = amax16<CAREFUL>(x);
-  const Cand k6 = make_cand<TAB>(div6(a), S_enc, S_dec, tab);
+  const Cand k6 = make_cand(div6(a), S_enc, tab);
   uint32_t c60, c61;
   encode16<CAREFUL>(x, k6.E, c60, c61);
   if (RECIPE == kNVFP4) {
@@ -335,7 +326,7 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
       e6 = err16<METRIC, PREC, ORDER>(x, t);
     }
     __builtin_amdgcn_sched_barrier(0);
-    const Cand k4 = make_cand<TAB>(a * 0.25f, S_enc, S_dec, tab);
+    const Cand k4 = make_cand(a * 0.25f, S_enc, tab);
     uint32_t c40, c41;
     encode16<CAREFUL>(x, k4.E, c40, c41);
     float e4;
@@ -356,11 +347,11 @@ __device__ __forceinline__ bool block_1x16(const float* x, float S_enc, float S_
 
 // Quantize a 1x16 block with the fast form, falling back to the careful form
 // when the block holds a NaN.
-template <int RECIPE, int METRIC, int PREC, int ORDER, bool NEED_XHAT, bool TAB>
+template <int RECIPE, int METRIC, int PREC, int ORDER, bool NEED_XHAT>
 __device__ __forceinline__ void quantize_block(const float* x, float S_enc, float S_dec, const Table& tab,
                                                BlockOut& o, float* xh) {
-  if (!block_1x16<RECIPE, METRIC, PREC, ORDER, false, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh))
-    block_1x16<RECIPE, METRIC, PREC, ORDER, true, NEED_XHAT, TAB>(x, S_enc, S_dec, tab, o, xh);
+  if (!block_1x16<RECIPE, METRIC, PREC, ORDER, false, NEED_XHAT>(x, S_enc, S_dec, tab, o, xh))
+    block_1x16<RECIPE, METRIC, PREC, ORDER, true, NEED_XHAT>(x, S_enc, S_dec, tab, o, xh);
 }
 
 // ------------------------------------------------------------ 1x16 kernel
@@ -502,12 +493,12 @@ __device__ __forceinline__ void unit_1x16(const Raw<DT>* raw, float S_enc, float
 #pragma unroll
     for (int j = 0; j < kNB; j++) {
       raw[j].unpack(x[j]);
-      fast_ok &= block_1x16<RECIPE, METRIC, PREC, ORDER, false, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
+      fast_ok &= block_1x16<RECIPE, METRIC, PREC, ORDER, false, false>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
     }
     if (!fast_ok) {
 #pragma unroll
       for (int j = 0; j < kNB; j++)
-        block_1x16<RECIPE, METRIC, PREC, ORDER, true, false, true>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
+        block_1x16<RECIPE, METRIC, PREC, ORDER, true, false>(x[j], S_enc, S_dec, tab, o[j], xh[j]);
     }
 #pragma unroll
     for (int j = 0; j < kNB; j++) {
@@ -520,7 +511,7 @@ __device__ __forceinline__ void unit_1x16(const Raw<DT>* raw, float S_enc, float
       float x[16], xh[16];
       raw[j].unpack(x);
       BlockOut o;
-      quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat, true>(x, S_enc, S_dec, tab, o, xh);
+      quantize_block<RECIPE, METRIC, PREC, ORDER, kXhat>(x, S_enc, S_dec, tab, o, xh);
       if (OUT == kOutQuant) {
         store_codes(U.out, off_c + j * 64 * 8, o.c0, o.c1);
         store_scale(U.scl, off_s + j * 64, o.scale);
@@ -753,7 +744,7 @@ __device__ __forceinline__ bool tile_rows(const Raw<DT>* raw, float S_enc, float
     a = __uint_as_float(pair_key_to_f32_bits<DT>(k));
   }
   a = group_max<kLPT>(a);
-  const Cand k6 = make_cand<true>(div6(a), S_enc, S_dec, tab);
+  const Cand k6 = make_cand(div6(a), S_enc, tab);
   if (RECIPE == kNVFP4) {
     float nan = 0.0f;
 #pragma unroll
@@ -767,7 +758,7 @@ __device__ __forceinline__ bool tile_rows(const Raw<DT>* raw, float S_enc, float
     scale = k6.scale;
     return CAREFUL || group_max<kLPT>(nan) == 0.0f;
   } else {
-    const Cand k4 = make_cand<true>(a * 0.25f, S_enc, S_dec, tab);
+    const Cand k4 = make_cand(a * 0.25f, S_enc, tab);
     float r6[kRPL], r4[kRPL];
     uint32_t c4[kRPL][2];
 #pragma unroll
@@ -1005,7 +996,7 @@ __global__ void __launch_bounds__(256) k_colwise(const Args16x16 args) {
 #pragma unroll
       for (int r = 0; r < 16; r++) x[r] = col_value<DT>(cur[r]);
       BlockOut o;
-      quantize_block<RECIPE, METRIC, PREC, ORDER, false, true>(x, S_enc, S_dec, tab, o, xh);
+      quantize_block<RECIPE, METRIC, PREC, ORDER, false>(x, S_enc, S_dec, tab, o, xh);
       cl[lane][bg] = (uint64_t)o.c0 | ((uint64_t)o.c1 << 32);
       sq[0] = __builtin_amdgcn_alignbit(sq[1], sq[0], 8);
       sq[1] = __builtin_amdgcn_alignbit(sq[2], sq[1], 8);
