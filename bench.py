@@ -1,29 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the four-over-six NVFP4 quantizer on one MI355X.
 
-One step is one pass of the hot path over the dense-activation workload
-(bf16 8192x4096 drawn from N(0,1), 1x16 blocks, per-tensor global scale,
-four-over-six with MSE exact error, E4M3 bound 448): the NaN-dropping tensor
-amax and the quantize writing packed E2M1 codes and E4M3 scales, in one
-launch (fos_quantize_fused). Inputs rotate over enough resident copies that
-the footprint exceeds the 256 MB Infinity Cache, so every step reads from HBM.
+One step is one pass of the hot path over the largest configuration, the
+grouped MoE activation quantize (pytorch/ao PR "Add the four-over-six grouped
+GEMM and dispatcher wiring", MoE commit): a packed bf16 token tensor of 65536
+rows plus 4096 over-allocated padding rows by 7168, split into 64 expert
+groups of Dirichlet(0.5) sizes rounded to 16 rows, each group N(0,1) times a
+factor 10^U(-2, 2). Each group's amax is expanded to per-row global scales
+and the whole tensor quantizes in one fos_quantize_grouped launch: 1x16
+blocks, four-over-six with MSE exact error, E4M3 bound 448, codes and scales
+written for all 69632 rows (the padding rows' as zero, never read). The
+group amaxes are the launch's input, computed on the device beforehand and
+not timed (the pages' precomputed-amax kernel metric); the one-launch form
+that computes them too is timed under `other_workloads`.
 
-`value` is the step's algorithmic HBM traffic over the measured step time.
-The step's kernel holds the tensor on chip between the amax and the
-quantize, so x is read once: 2 B/elem in, 0.5 + 1/16 B/elem out. The
-`roofline`
-object covers the step's kernel, timed with HIP events on the stream it runs
-on. `cpu_baseline` times the CPU oracle on the same workload. The quantize
-kernel alone with a precomputed amax (the pages' kernel metric), the
-two-launch step and the other configurations (16x16 weights, the fused-QDQ
-expert list, the grouped MoE tensor) are timed briefly and reported under
-`other_workloads`.
+`value` is the step's algorithmic HBM traffic (the data rows read once, 2 B
+per element; codes and scales of every row written, 0.5625 B per element)
+over the measured step time; the data rows alone exceed the 256 MB Infinity
+Cache four times over, so every step reads from HBM. `roofline` covers the
+step's kernel, timed with HIP events on the stream it runs on, beside a
+hand-written streaming kernel of the same read:write mix (bench_stream.hip).
+`cpu_baseline` times the CPU oracle on the same tensor and checks the GPU's
+output against it in full. The other configurations (the dense activation
+tensor, the 16x16 weights, the fused-QDQ expert list, the streaming
+ceilings) are timed briefly under `other_workloads`, each in algorithmic
+bytes (every input read once, every output written once).
 
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -34,23 +42,47 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public spec
-PEAK_VALU_LANE_TPS = 256 * 64 * 2.4e9  # VALU lane-instructions/s: 256 CUs x 64 lanes x 2.4 GHz
+N_SIMD = 256 * 4               # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9               # peak engine clock
 MALL_BYTES = 256 << 20
 FOOTPRINT = 1 << 30            # rotate buffers up to >= 1 GiB
 METRIC = "4over6 quantize/QDQ achieved HBM GB/s and % of MI355X peak (bit-exact)"
-FUSED_KERNEL = "void fos::k_fused_onchip<0, 1, 1, 0, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)"
-QUANT_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0, 0>(fos::Args1x16<1>)"
 COPY_BYTES = 256 << 20         # the profile pass's calibration copy
-# counter summaries per kernel: (file, readable workload, algorithmic bytes per launch)
-_N = 8192 * 4096
-COUNTER_FILES = {
-    FUSED_KERNEL: (os.path.join(ROOT, "profiles", "fused_amax_quantize_bf16_8192x4096_counters.txt"),
-                   "fos_quantize_fused: per-tensor amax and quantize in one launch, one read of x", _N * 2 + _N // 2 + _N // 16),
-    QUANT_KERNEL: (os.path.join(ROOT, "profiles", "quantize_1x16_bf16_8192x4096_counters.txt"),
-                   "fos_quantize with a precomputed amax", _N * 2 + _N // 2 + _N // 16),
+
+# the grouped MoE workload
+M5, PAD5, K5, G5 = 65536, 4096, 7168, 64
+STEP_BYTES = M5 * K5 * 2 + (M5 + PAD5) * (K5 // 2 + K5 // 16)
+KNOBS = dict(recipe="4over6", err_metric="mse", err_prec="exact", bound=448)
+
+HEADLINE_KERNEL = "void fos::k_1x16<1, 0, 1, 1, 0, 0, 2, 0>(fos::Args1x16<1>)"
+_N2 = 8192 * 4096
+# kernels with a counter summary: (file stem, readable workload, algorithmic bytes per launch)
+COUNTER_KERNELS = {
+    HEADLINE_KERNEL: ("quantize_grouped_bf16_65536x7168",
+                      "fos_quantize_grouped, bf16 65536 (+4096 padding) x 7168, 64 groups, four-over-six MSE exact, "
+                      "bound 448", STEP_BYTES),
+    "void fos::k_16x16<0, 1, 1, 0, 0, 0>(fos::Args16x16)":
+        ("quantize_16x16_bf16_4096x14336",
+         "fos_quantize 16x16 tiles, bf16 4096x14336 0.02*N(0,1), per-tensor, four-over-six MSE exact, bound 448",
+         4096 * 14336 * 2 + 4096 * 14336 // 2 + 4096 * 14336 // 16),
+    "void fos::k_1x16<48, 0, 1, 1, 1, 0, 0, 1>(fos::Args1x16<48>)":
+        ("qdq_list_bf16_8x2048x7168",
+         "fos_qdq_list, 8 x bf16 2048x7168 expert weights, four-over-six MSE FP16-error, bound 448",
+         8 * 2048 * 7168 * 4),
+    "void fos::k_fused_onchip<0, 1, 1, 0, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)":
+        ("fused_amax_quantize_bf16_8192x4096",
+         "fos_quantize_fused (amax and quantize in one launch, x read once), bf16 8192x4096 N(0,1), four-over-six "
+         "MSE exact, bound 448", _N2 * 2 + _N2 // 2 + _N2 // 16),
+    "void fos::k_1x16<1, 0, 1, 1, 0, 0, 0, 0>(fos::Args1x16<1>)":
+        ("quantize_1x16_bf16_8192x4096",
+         "fos_quantize with a precomputed amax, bf16 8192x4096 N(0,1), four-over-six MSE exact, bound 448",
+         _N2 * 2 + _N2 // 2 + _N2 // 16),
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_adaptive_block_amd", "csrc", f)
                   for f in ("fos_kernels.hip", "fos_device.h", "fos_kernels.h")]
+PROFILES = os.path.join(ROOT, "profiles")
+HEADLINE_TRACE = os.path.join(PROFILES, "kernel_trace_quantize_grouped_bf16_65536x7168.txt")
+STREAM_LIB = os.path.join(ROOT, "libbench_stream.so")
 
 
 def kernel_source_hash() -> str:
@@ -58,9 +90,6 @@ def kernel_source_hash() -> str:
     for p in KERNEL_SOURCES:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
-
-
-KERNEL_TRACE = os.path.join(ROOT, "profiles", "kernel_trace_bench_workloads.txt")
 
 
 def read_profile_value(path, key):
@@ -82,64 +111,124 @@ def read_profile_value(path, key):
         return None
 
 
-def read_counters(kernel):
-    """HBM bytes per launch of `kernel` from its committed rocprofv3 counter
-    summary, or None when it is missing or was taken on other kernel code."""
-    return read_profile_value(COUNTER_FILES[kernel][0], "hbm_bytes_per_launch")
+def counter_file(kernel):
+    return os.path.join(PROFILES, f"counters_{COUNTER_KERNELS[kernel][0]}.txt")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def rotating(t, n_bytes_per_set, extra_per_set=0):
-    import torch
-    per = n_bytes_per_set + extra_per_set
-    n = max(2, -(-FOOTPRINT // per))
-    return [t.clone() for _ in range(n)] if t is not None else [None] * n
+def rotating(t, bytes_per_set):
+    n = max(2, -(-FOOTPRINT // bytes_per_set))
+    return [t.clone() for _ in range(n)]
 
 
 def time_loop(fn, n_sets, steps, warmup):
-    """Run fn(i) for warmup untimed and `steps` timed iterations on the current
-    stream; returns (total_ms, per-launch ms list from events around fn)."""
+    """Run fn(i) `warmup` times untimed, then `steps` times with an event pair
+    around each launch on the current stream; returns the per-launch ms."""
     import torch
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
     for i in range(steps):
         evs[i][0].record()
         fn(i % n_sets)
         evs[i][1].record()
-    end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end), [a.elapsed_time(b) for a, b in evs]
+    return [a.elapsed_time(b) for a, b in evs]
 
+
+def gbs(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def entry(nbytes, ms, **extra):
+    g = gbs(nbytes, ms)
+    return {"avg_launch_us": round(ms * 1e3, 2), "GB/s": g, "frac": round(g / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": int(nbytes), **extra}
+
+
+# ---------------------------------------------------------------- workloads
+
+def grouped_inputs(torch, fos, synthdata):
+    """The grouped MoE tensor on the device, its offsets and its group amaxes
+    (computed on the device: input preparation, not part of the step)."""
+    import numpy as np
+    x, offs, _ = synthdata.grouped_tokens(M5, PAD5, K5, G5)
+    xd = x.to("cuda")
+    od = torch.from_numpy(offs).to("cuda")
+    starts = np.concatenate([[0], offs[:-1]])
+    gam = torch.zeros(G5, dtype=torch.float32, device="cuda")
+    for g, (s, e) in enumerate(zip(starts, offs)):
+        if e > s:
+            fos.fos_amax(xd[s:e], "tensor", out=gam[g:g + 1])
+    return x, offs, xd, od, gam
+
+
+class Stream:
+    """The hand-written streaming kernels of bench_stream.hip."""
+
+    MIXES = {"read_only": 0, "write_only": 1, "quantize_mix": 2, "qdq_mix": 3}
+
+    def __init__(self):
+        if not os.path.exists(STREAM_LIB):
+            raise FileNotFoundError(f"{STREAM_LIB} is not built (run __graft_entry__.build())")
+        self.lib = ctypes.CDLL(STREAM_LIB)
+        self.lib.stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.stream_bytes_per_unit.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                                   ctypes.POINTER(ctypes.c_int64)]
+
+    def measure(self, torch, np, mix, units, steps=60, warmup=10):
+        """Best median GB/s over the two store policies, and each."""
+        r, w = ctypes.c_int64(), ctypes.c_int64()
+        self.lib.stream_bytes_per_unit(self.MIXES[mix], ctypes.byref(r), ctypes.byref(w))
+        src = torch.empty(max(1, units * r.value), dtype=torch.uint8, device="cuda")
+        dst = torch.empty(max(1, units * w.value), dtype=torch.uint8, device="cuda")
+        src.random_(0, 255) if r.value else None
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nbytes = units * (r.value + w.value)
+        out = {}
+        for nt in (0, 1):
+            def run(_i, nt=nt):
+                rc = self.lib.stream_run(self.MIXES[mix], nt, ctypes.c_void_p(src.data_ptr()),
+                                         ctypes.c_void_p(dst.data_ptr()), units, ctypes.c_void_p(sink.data_ptr()),
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                assert rc == 0
+            ms = float(np.median(time_loop(run, 1, steps, warmup)))
+            out["nt" if nt else "default"] = entry(nbytes, ms)
+        best = max(out.values(), key=lambda e: e["GB/s"])
+        return {"GB/s": best["GB/s"], "frac": best["frac"], "read_bytes": units * r.value,
+                "write_bytes": units * w.value, "stores": out}
+
+
+# ---------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    # 400 untimed steps (about 12 ms): after 20 the clocks are still rising
-    # and the step measures about 1 us slower
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=200)
+    # untimed steps first: the clocks take about 12 ms to settle
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads")
     ap.add_argument("--profile-pass", action="store_true",
-                    help="short run for rocprofv3: a few quantize launches and a known-size copy, no JSON")
+                    help="short run for rocprofv3: each counter-summary workload, then a known-size copy; no JSON")
     ap.add_argument("--write-profiles", metavar="DIR",
-                    help="summarize rocprofv3 CSV output under DIR (kt/, fetch/, write/, sq/) into profiles/")
+                    help="summarize rocprofv3 CSV output under DIR (kt/, kt_pass/, fetch/, write/, sq/, occ/)")
+    ap.add_argument("--profiles-out", metavar="DIR", default=PROFILES,
+                    help="where --write-profiles writes its summaries (default: profiles/)")
     args = ap.parse_args()
     if args.write_profiles:
-        write_profiles(args.write_profiles)
+        write_profiles(args.write_profiles, args.profiles_out)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
-              "the quantizer's step has no cross-GPU part, so it is measured on one GPU only",
+              "every GPU box here has one GPU, and the quantizer's step has no cross-GPU part",
               file=sys.stderr)
         sys.exit(2)
 
@@ -151,130 +240,55 @@ def main():
     from synthdata import raw_bits
 
     torch.cuda.set_device(0)
-    M, K = 8192, 4096
-    n = M * K
-    knobs = dict(recipe="4over6", block="1x16", scale_gran="tensor", err_metric="mse", err_prec="exact", bound=448)
-    log(f"[bench] generating bf16 {M}x{K} N(0,1) (seed 21)")
-    x_host = synthdata.activation_family("normal", M, K, 21, "bf16")
-    x0 = x_host.to("cuda")
-    in_bytes = n * 2
-    out_bytes = n // 2 + n // 16
-    xs = rotating(x0, in_bytes, out_bytes)
-    nset = len(xs)
-    codes = [torch.empty(M, K // 2, dtype=torch.uint8, device="cuda") for _ in range(nset)]
-    scales = [torch.empty(M, K // 16, dtype=torch.uint8, device="cuda") for _ in range(nset)]
-    sdec = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(nset)]
-    amax = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(nset)]
-    log(f"[bench] {nset} rotating buffer sets ({nset * (in_bytes + out_bytes) / 2**30:.2f} GiB)")
-
-    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
-    status = torch.zeros(1, dtype=torch.int32, device="cuda")
-
-    def step(i):
-        fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=amax[i], sdec=sdec[i], workspace=ws,
-                               status=status, **knobs)
-
     if args.profile_pass:
-        # a few launches of the step's kernel and of the separate amax and
-        # quantize kernels, plus a plain copy of known size for calibrating
-        # the HBM counters
-        for i in range(8):
-            step(i % nset)
-        for i in range(8):
-            fos.fos_amax(xs[i % nset], "tensor", out=amax[i % nset])
-            fos.fos_quantize(xs[i % nset], amax[i % nset], codes=codes[i % nset], scales=scales[i % nset],
-                             sdec=sdec[i % nset], **knobs)
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] profile pass done (copy kernel: {COPY_BYTES} bytes read and written per launch)")
+        profile_pass(fos, synthdata, torch, np)
         return
 
-    # ---------------------------------------------------------------- main step
+    log(f"[bench] generating the grouped MoE tensor bf16 {M5}+{PAD5}x{K5}, {G5} groups (seeds 51-54)")
+    x_host, offs, xd, od, gam = grouped_inputs(torch, fos, synthdata)
+    codes = torch.empty(M5 + PAD5, K5 // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M5 + PAD5, K5 // 16, dtype=torch.uint8, device="cuda")
+    gsdec = torch.empty(G5, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(_i=0):
+        fos.fos_quantize_grouped(xd, od, gam, codes=codes, scales=scales, group_sdec=gsdec, status=status, **KNOBS)
+
+    # ---------------------------------------------------------------- the step
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
-    for i in range(args.warmup):
-        step(i % nset)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     # the step is one kernel launch: two events on the launch stream bracket
     # the timed region, and the kernel's average launch time is the region's
     # time over the step count (per-step events would add their own packets)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(args.steps):
-        step((args.warmup + i) % nset)
+    for _ in range(args.steps):
+        step()
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    k_avg_ms = ms_per_step
-    barrier_ok = int(status.item()) == 0
-    # the step's kernel reads x once (the amax and the quantize share that
-    # read) and writes codes and scales: 2 + 0.5 + 1/16 B per element
-    step_bytes = in_bytes + out_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    k_gbs = step_bytes / (k_avg_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s); fused kernel {k_avg_ms * 1e3:.1f} us "
-        f"({k_gbs:.0f} GB/s, {k_gbs / PEAK_HBM_GBS:.1%} of peak); barrier ok: {barrier_ok}")
-
-    # bit-exact spot check of the last outputs against the CPU oracle
-    bit_exact = None
-    try:
-        import oracle
-        orc = oracle.get()
-        last = (args.warmup + args.steps - 1) % nset
-        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(0).integers(0, M, 62)]))
-        a_host = orc.amax(raw_bits(x_host), "bf16", "tensor")
-        want = orc.quantize(raw_bits(x_host)[rows], "bf16", a_host, **knobs)
-        got_c = codes[last].cpu().numpy()[rows]
-        got_s = scales[last].cpu().numpy()[rows]
-        got_a = amax[last].cpu().numpy()
-        bit_exact = bool(np.array_equal(got_c, want["codes"]) and np.array_equal(got_s, want["scales"])
-                         and got_a.view(np.uint32)[0] == a_host.view(np.uint32)[0])
-        log(f"[bench] bit-exact vs oracle on {rows.size} sampled rows and the amax: {bit_exact}")
-    except Exception as e:  # the oracle is optional for timing
-        log(f"[bench] oracle spot check skipped: {e}")
+    ms_per_step = start.elapsed_time(end) / args.steps
+    value = STEP_BYTES / (ms_per_step * 1e-3) / 1e9
+    ok_status = int(status.item()) == 0
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us: {value:.0f} GB/s, {value / PEAK_HBM_GBS:.1%} of 8 TB/s; "
+        f"status clean: {ok_status}")
 
     # ---------------------------------------------------------------- CPU oracle
-    cpu = None
+    cpu, bit_exact = None, None
     if not args.no_cpu_baseline:
-        import oracle
-        orc = oracle.get()
-        xb = raw_bits(x_host)
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            a_h = orc.amax(xb, "bf16", "tensor")
-            orc.quantize(xb, "bf16", a_h, **knobs)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or el > 30:
-                break
-        cpu = {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
-               "kind": "oracle",
-               "sample": f"{reps} full steps (amax + quantize of the whole bf16 {M}x{K} tensor) in {el:.1f} s"}
-        log(f"[bench] CPU oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+        cpu, bit_exact = cpu_leg(args, x_host, offs, gam, codes, scales, raw_bits, np)
 
-    # ---------------------------------------------------------------- other workloads
+    # ---------------------------------------------------------------- ceilings and other workloads
+    stream = Stream()
+    ceiling = stream.measure(torch, np, "quantize_mix", M5 * K5 * 2 // 4096)  # the step's read bytes
+    log(f"[bench] streaming ceiling at the quantize mix (2 : 0.5625): {ceiling['GB/s']:.0f} GB/s")
     other = {}
     if not args.no_other:
-        other = other_workloads(fos, synthdata, torch, np, c2=(xs, codes, scales, amax, sdec, knobs))
+        other = other_workloads(fos, synthdata, torch, np, stream, (xd, od, gam, codes, scales))
 
-    traffic = read_counters(FUSED_KERNEL)
-    rocprof_us = read_profile_value(KERNEL_TRACE, "fused_kernel_avg_us")
-    # the VALU co-bound beside the HBM one: the kernel's VALU wave
-    # instructions (SQ_INSTS_VALU of the committed counter pass) as lane
-    # instructions per second against 256 CUs x 64 lanes x 2.4 GHz
-    cf = COUNTER_FILES[FUSED_KERNEL][0]
-    wave_insts = read_profile_value(cf, "sq_insts_valu")
-    valu = None
-    if wave_insts:
-        lane_rate = wave_insts * 64 / (k_avg_ms * 1e-3)
-        valu = {"lane_insts_per_launch": int(wave_insts * 64),
-                "lane_insts_per_element": read_profile_value(cf, "valu_lane_insts_per_element"),
-                "cvt_insts_per_block": read_profile_value(cf, "valu_cvt_insts_per_block"),
-                "achieved": round(lane_rate / 1e12, 2), "peak": PEAK_VALU_LANE_TPS / 1e12,
-                "unit": "T lane-instructions/s", "frac": round(lane_rate / PEAK_VALU_LANE_TPS, 4)}
+    traffic = read_profile_value(counter_file(HEADLINE_KERNEL), "hbm_bytes_per_launch")
+    rocprof_us = read_profile_value(HEADLINE_TRACE, "headline_kernel_avg_us")
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -288,38 +302,274 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "dense activation quantize, bf16 8192x4096 N(0,1) seed 21, 1x16 blocks, "
-                               "per-tensor amax + four-over-six MSE exact, E4M3 bound 448, in one launch "
-                               "(fos_quantize_fused)",
-                   "M": M, "K": K, "input_dtype": "bf16", "recipe": "4over6", "err_metric": "mse",
-                   "err_prec": "exact", "e4m3_bound": 448, "rotating_sets": nset,
-                   "step_bytes": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "fos_quantize_fused (k_fused_onchip, bf16, 4over6 MSE exact)",
-                     "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": round(k_avg_ms * 1e3, 2),
-                     "rocprof_kernel_avg_us": rocprof_us},
-        "valu": valu,
-        "barrier_ok": barrier_ok,
-        "bit_exact_sample": bit_exact,
+        "config": {"workload": f"grouped MoE activation quantize: bf16 {M5} (+{PAD5} padding) x {K5} tokens in "
+                               f"{G5} groups (Dirichlet(0.5) sizes in multiples of 16 rows, group factors "
+                               "10^U(-2,2), seeds 51-54), per-group amax expanded per row, 1x16 blocks, "
+                               "four-over-six MSE exact, E4M3 bound 448, one fos_quantize_grouped launch",
+                   "M": M5, "pad_rows": PAD5, "K": K5, "groups": G5, "input_dtype": "bf16", "recipe": "4over6",
+                   "err_metric": "mse", "err_prec": "exact", "e4m3_bound": 448, "step_bytes": STEP_BYTES},
+        "roofline": roofline(ms_per_step, traffic, rocprof_us, ceiling),
+        "status_clean": ok_status,
+        "bit_exact": bit_exact,
         "cpu_baseline": cpu,
         "other_workloads": other,
     }
     print(json.dumps(result), flush=True)
 
 
+def roofline(ms, traffic, rocprof_us, ceiling):
+    achieved = STEP_BYTES / (ms * 1e-3) / 1e9
+    cf = counter_file(HEADLINE_KERNEL)
+    valu = None
+    insts = read_profile_value(cf, "sq_insts_valu")
+    if insts:
+        # the VALU co-bound from the kernel's own counters: VALUBusy is the
+        # fraction of each SIMD's cycles with a VALU instruction in flight;
+        # SQ_ACTIVE_INST_VALU (quad-cycles) over SQ_INSTS_VALU gives the
+        # measured issue cycles per wave instruction (converts included)
+        valu = {"valu_busy": read_profile_value(cf, "valu_busy"),
+                "valu_cycles_per_simd": read_profile_value(cf, "valu_cycles_per_simd"),
+                "cycles_per_valu_inst": read_profile_value(cf, "cycles_per_valu_inst"),
+                "valu_time_at_peak_clock_us": read_profile_value(cf, "valu_time_at_peak_clock_us"),
+                "wave_insts_per_launch": int(insts),
+                "cvt_wave_insts_per_launch": read_profile_value(cf, "sq_insts_valu_cvt"),
+                "lane_insts_per_block": read_profile_value(cf, "valu_lane_insts_per_block"),
+                "occupancy_waves_per_simd": read_profile_value(cf, "occupancy_waves_per_simd")}
+    return {"bound": "hbm", "kernel": "fos_quantize_grouped (k_1x16 grouped, bf16, 4over6 MSE exact)",
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": STEP_BYTES, "avg_launch_us": round(ms * 1e3, 2),
+            "rocprof_kernel_avg_us": rocprof_us,
+            "ceiling_same_mix_GBs": ceiling["GB/s"], "frac_of_ceiling": round(achieved / ceiling["GB/s"], 4),
+            "valu": valu}
+
+
+def cpu_leg(args, x_host, offs, gam_dev, codes, scales, raw_bits, np):
+    """The oracle on the same tensor: its group amaxes, then its grouped
+    quantize, timed; the GPU's group amaxes, codes and scales are compared
+    with the oracle's in full."""
+    import oracle
+    orc = oracle.get()
+    bits = raw_bits(x_host)
+    starts = np.concatenate([[0], offs[:-1]])
+    log("[bench] CPU oracle: group amaxes")
+    gam = np.array([orc.amax(bits[s:e], "bf16", "tensor")[0] if e > s else 0.0 for s, e in zip(starts, offs)],
+                   np.float32)
+    reps, t0, want = 0, time.perf_counter(), None
+    while True:
+        want = orc.quantize_grouped(bits, "bf16", offs, gam, **KNOBS)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or el > 30:
+            break
+    cpu = {"value": round(STEP_BYTES * reps / el / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+           "kind": "oracle",
+           "sample": f"{reps} full steps (the grouped quantize of the whole bf16 {M5}+{PAD5}x{K5} tensor, group "
+                     f"amaxes given) in {el:.1f} s"}
+    log(f"[bench] CPU oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+    same = (np.array_equal(gam_dev.cpu().numpy().view(np.uint32), gam.view(np.uint32))
+            and np.array_equal(codes.cpu().numpy(), want["codes"]) and np.array_equal(scales.cpu().numpy(),
+                                                                                     want["scales"]))
+    log(f"[bench] bit-exact vs the oracle (group amaxes, all codes and scales): {same}")
+    return cpu, bool(same)
+
+
+def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
+    """Brief kernel-only timings of the other configurations; each figure is
+    the median launch of its loop, over the algorithmic bytes: every input
+    read once and every output written once."""
+    out = {}
+    xd, od, gam, c, s = c5
+
+    # ceilings: the hand-written streams (>= 1 GiB footprints) and torch's copy
+    for mix in ("read_only", "write_only", "qdq_mix"):
+        out[f"stream_{mix}"] = stream.measure(torch, np, mix, 262144)
+        log(f"[bench] stream {mix}: {out[f'stream_{mix}']['GB/s']:.0f} GB/s")
+    srcs = [torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    ms = float(np.median(time_loop(lambda i: dsts[i].copy_(srcs[i]), 4, 50, 5)))
+    out["torch_copy_256MiB"] = entry(2 * COPY_BYTES, ms)
+    del srcs, dsts
+
+    # the grouped MoE tensor: bound 256, and the group amaxes in the same launch
+    ms = float(np.median(time_loop(lambda i: fos.fos_quantize_grouped(xd, od, gam, codes=c, scales=s, recipe="4over6",
+                                                                      err_metric="mse", bound=256), 1, steps, warmup)))
+    out[f"quantize_grouped_{M5}+{PAD5}x{K5}_G{G5}_256"] = entry(STEP_BYTES, ms)
+    ga = torch.empty(G5, dtype=torch.float32, device="cuda")
+    ms = float(np.median(time_loop(lambda i: fos.fos_quantize_grouped_fused(xd, od, codes=c, scales=s, group_amax=ga,
+                                                                            **KNOBS), 1, steps, warmup)))
+    out[f"fused_group_amax_quantize_grouped_{M5}+{PAD5}x{K5}_G{G5}_448"] = entry(
+        STEP_BYTES, ms, note="one launch; its amax phase reads the data rows a second time")
+    log(f"[bench] grouped: {out}")
+
+    # the dense activation tensor, bf16 8192x4096 N(0,1), rotated over >= 1 GiB
+    M, K = 8192, 4096
+    n = M * K
+    x0 = synthdata.activation_family("normal", M, K, 21, "bf16").to("cuda")
+    qb = n * 2 + n // 2 + n // 16
+    xs = rotating(x0, qb)
+    ns = len(xs)
+    codes = [torch.empty(M, K // 2, dtype=torch.uint8, device="cuda") for _ in range(ns)]
+    scales = [torch.empty(M, K // 16, dtype=torch.uint8, device="cuda") for _ in range(ns)]
+    amax = [fos.fos_amax(x, "tensor") for x in xs]
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    knobs = dict(KNOBS)
+    runs = {
+        "fused_amax_quantize_bf16_8192x4096": (
+            lambda i: fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=amax[i], workspace=ws,
+                                             status=st, **knobs), qb, "one launch, x read once"),
+        "quantize_1x16_bf16_8192x4096_precomputed_amax": (
+            lambda i: fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], **knobs), qb, None),
+        "amax_then_quantize_bf16_8192x4096": (
+            lambda i: (fos.fos_amax(xs[i], "tensor", out=amax[i]),
+                       fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], **knobs)), qb,
+            "two launches; x read twice"),
+    }
+    row_amax = [fos.fos_amax(x, "row") for x in xs]
+    ra = torch.empty(M, dtype=torch.float32, device="cuda")
+    rk = dict(knobs, scale_gran="row")
+    runs["quantize_1x16_bf16_8192x4096_per_row_amax"] = (
+        lambda i: fos.fos_quantize(xs[i], row_amax[i], codes=codes[i], scales=scales[i], **rk), qb, None)
+    runs["fused_row_amax_quantize_bf16_8192x4096"] = (
+        lambda i: fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=ra, **rk), qb,
+        "one launch, each row read once")
+    ct = torch.empty(K, M // 2, dtype=torch.uint8, device="cuda")
+    stt = torch.empty(K, M // 16, dtype=torch.uint8, device="cuda")
+    runs["quantize_columnwise_bf16_8192x4096"] = (
+        lambda i: fos.fos_quantize_columnwise(xs[i], amax[i], codes=ct, scales=stt, **knobs), qb, None)
+    sd = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(ns)]
+    for i in range(ns):
+        fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sd[i], **knobs)
+    ys = [torch.empty_like(x) for x in xs]
+    runs["dequantize_bf16_8192x4096"] = (
+        lambda i: fos.nvfp4_dequantize(codes[i], scales[i], sd[i], "tensor", torch.bfloat16, out=ys[i]), qb, None)
+    qkw = dict(recipe="4over6", err_metric="mse", err_prec="fp16", bound=448)
+    runs["fused_amax_qdq_bf16_8192x4096_mse_fp16_448"] = (
+        lambda i: fos.fos_qdq_fused(xs[i], out=ys[i], amax=amax[i], workspace=ws, status=st, **qkw), 4 * n,
+        "one launch, x read once")
+    runs["amax_then_qdq_bf16_8192x4096_mse_fp16_448"] = (
+        lambda i: (fos.fos_amax(xs[i], "tensor", out=amax[i]), fos.fos_qdq(xs[i], amax[i], out=ys[i], **qkw)), 4 * n,
+        "two launches; x read twice")
+    for key, (fn, nbytes, note) in runs.items():
+        ms = float(np.median(time_loop(fn, ns, 200, 10)))
+        out[key] = entry(nbytes, ms, **({"note": note} if note else {}))
+        log(f"[bench] {key}: {out[key]['avg_launch_us']} us, {out[key]['GB/s']} GB/s")
+    del xs, codes, scales, ys, row_amax, ct, stt
+
+    # 16x16 weights, bf16 4096x14336 and fp32 4096x4096, per-tensor, MSE exact, 448
+    for dtype, (M, K) in (("bf16", (4096, 14336)), ("fp32", (4096, 4096))):
+        w = synthdata.weight(M, K, 31 if dtype == "bf16" else 32, dtype).to("cuda")
+        a = fos.fos_amax(w, "tensor")
+        eb = 2 if dtype == "bf16" else 4
+        nbytes = M * K * eb + M * K // 2 + M * K // 16
+        wsets = rotating(w, nbytes)
+        cc = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+        ss = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
+        ms = float(np.median(time_loop(lambda i: fos.fos_quantize(wsets[i], a, codes=cc, scales=ss, block="16x16",
+                                                                  **knobs), len(wsets), steps, warmup)))
+        out[f"quantize_16x16_{dtype}_{M}x{K}"] = entry(nbytes, ms)
+        log(f"[bench] 16x16 {dtype}: {out[f'quantize_16x16_{dtype}_{M}x{K}']}")
+        del wsets, w
+
+    # fused QDQ over the 8 expert weights 2048x7168, bf16 and fp16, the five
+    # timed modes, each list rotated over >= 1 GiB (3 copies)
+    lst = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=("bf16", "fp16"))
+    for dtype in ("bf16", "fp16"):
+        base = [t.to("cuda") for t in lst[dtype]]
+        nbytes = sum(t.numel() for t in base) * 4
+        nsets = max(3, -(-FOOTPRINT // nbytes))
+        sets = [[t.clone() for t in base] for _ in range(nsets)]
+        ams = [[fos.fos_amax(t, "tensor") for t in xs_] for xs_ in sets]
+        ys = [[torch.empty_like(t) for t in xs_] for xs_ in sets]
+        for r, m, p, bnd in (("nvfp4", "mse", "fp16", 448), ("4over6", "mae", "fp16", 448),
+                             ("4over6", "mae", "fp16", 256), ("4over6", "mse", "fp16", 448),
+                             ("4over6", "mse", "fp16", 256)):
+            ms = float(np.median(time_loop(lambda i: fos.fos_qdq_list(sets[i], ams[i], outs=ys[i], recipe=r,
+                                                                      err_metric=m, err_prec=p, bound=bnd),
+                                           nsets, steps, warmup)))
+            key = f"qdq_list_8x2048x7168_{dtype}_{r}" + ("" if r == "nvfp4" else f"_{m}_{p}_{bnd}")
+            out[key] = entry(nbytes, ms, rotating_sets=nsets)
+            log(f"[bench] {key}: {out[key]['avg_launch_us']} us, {out[key]['GB/s']} GB/s")
+        del sets, ys, ams, base
+    return out
+
+
+# ---------------------------------------------------------------- profile pass
+
+def profile_pass(fos, synthdata, torch, np):
+    """A few launches of each kernel with a counter summary, each workload's
+    buffers rotated over >= 1 GiB, then a plain copy of known size that
+    calibrates the HBM counters."""
+    reps = 10
+    _, _, xd, od, gam = grouped_inputs(torch, fos, synthdata)
+    c = torch.empty(M5 + PAD5, K5 // 2, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M5 + PAD5, K5 // 16, dtype=torch.uint8, device="cuda")
+    for _ in range(reps):
+        fos.fos_quantize_grouped(xd, od, gam, codes=c, scales=s, **KNOBS)
+    torch.cuda.synchronize()
+    del xd, c, s
+
+    w = synthdata.weight(4096, 14336, 31, "bf16").to("cuda")
+    a = fos.fos_amax(w, "tensor")
+    wsets = rotating(w, COUNTER_KERNELS["void fos::k_16x16<0, 1, 1, 0, 0, 0>(fos::Args16x16)"][2])
+    c = torch.empty(4096, 14336 // 2, dtype=torch.uint8, device="cuda")
+    s = torch.empty(4096, 14336 // 16, dtype=torch.uint8, device="cuda")
+    for i in range(reps):
+        fos.fos_quantize(wsets[i % len(wsets)], a, codes=c, scales=s, block="16x16", **KNOBS)
+    torch.cuda.synchronize()
+    del wsets, w, c, s
+
+    base = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=("bf16",))["bf16"]
+    sets = [[t.to("cuda") for t in base] for _ in range(3)]
+    ams = [[fos.fos_amax(t, "tensor") for t in xs_] for xs_ in sets]
+    ys = [[torch.empty_like(t) for t in xs_] for xs_ in sets]
+    for i in range(reps):
+        fos.fos_qdq_list(sets[i % 3], ams[i % 3], outs=ys[i % 3], recipe="4over6", err_metric="mse", err_prec="fp16",
+                         bound=448)
+    torch.cuda.synchronize()
+    del sets, ams, ys
+
+    M, K = 8192, 4096
+    x0 = synthdata.activation_family("normal", M, K, 21, "bf16").to("cuda")
+    xs = rotating(x0, _N2 * 2 + _N2 // 2 + _N2 // 16)
+    ns = len(xs)
+    codes = [torch.empty(M, K // 2, dtype=torch.uint8, device="cuda") for _ in range(ns)]
+    scales = [torch.empty(M, K // 16, dtype=torch.uint8, device="cuda") for _ in range(ns)]
+    amax = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(ns)]
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    for i in range(reps):
+        fos.fos_quantize_fused(xs[i % ns], codes=codes[i % ns], scales=scales[i % ns], amax=amax[i % ns],
+                               workspace=ws, **KNOBS)
+    for i in range(reps):
+        fos.fos_quantize(xs[i % ns], amax[i % ns], codes=codes[i % ns], scales=scales[i % ns], **KNOBS)
+    torch.cuda.synchronize()
+    del xs, codes, scales
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] profile pass done (copy kernel: {COPY_BYTES} bytes read and written per launch)")
+
+
 # ---------------------------------------------------------------- profile summaries
 
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o kt -- "
-          "python3 $REPO/bench.py --steps 200 --no-cpu-baseline",
-    "fetch": "timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o fetch -- "
+          "python3 $REPO/bench.py --no-cpu-baseline --no-other",
+    "kt_pass": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt_pass -o kt_pass -- "
+               "python3 $REPO/bench.py --profile-pass",
+    "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o fetch -- "
              "python3 $REPO/bench.py --profile-pass",
-    "write": "timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o write -- "
+    "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o write -- "
              "python3 $REPO/bench.py --profile-pass",
-    "sq": "timeout -s KILL 90 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES "
-          "SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VALU_CVT GRBM_GUI_ACTIVE --output-format csv "
+    "sq": "timeout -s KILL 120 rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_CVT SQ_ACTIVE_INST_VALU "
+          "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE --output-format csv "
           "-d $OUT/sq -o sq -- python3 $REPO/bench.py --profile-pass",
+    "occ": "timeout -s KILL 120 rocprofv3 --pmc OccupancyPercent VALUBusy --output-format csv "
+           "-d $OUT/occ -o occ -- python3 $REPO/bench.py --profile-pass",
 }
 _DT = {"0": "bf16", "1": "fp16", "2": "fp32"}
 _RC = {"0": "nvfp4", "1": "4over6"}
@@ -327,8 +577,6 @@ _MT = {"0": "mae", "1": "mse"}
 _PR = {"0": "exact", "1": "fp16err"}
 _GR = {"0": "tensor", "1": "row", "2": "grouped"}
 _OUT = {"0": "quantize", "1": "qdq"}
-
-
 _ORD = {"0": "", "1": " seq"}
 
 
@@ -352,16 +600,11 @@ def describe_kernel(name: str) -> str:
         err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
         form = " (one read)" if form else " (two reads)"
         return f"fused amax + 1x16 {_OUT[out or '0']}{form} {_DT[dt]} {_RC[rc]}{err} tensor"
-    m = re.match(r"void fos::k_fused_row<(\d), (\d), (\d), (\d), (\d)>", name)
+    m = re.match(r"void fos::k_fused_(row|grouped)<(\d), (\d), (\d), (\d), (\d)>", name)
     if m:
-        dt, rc, mt, pr, od = m.groups()
+        kind, dt, rc, mt, pr, od = m.groups()
         err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
-        return f"fused per-row amaxes + 1x16 quantize {_DT[dt]} {_RC[rc]}{err} row"
-    m = re.match(r"void fos::k_fused_grouped<(\d), (\d), (\d), (\d), (\d)>", name)
-    if m:
-        dt, rc, mt, pr, od = m.groups()
-        err = f" {_MT[mt]} {_PR[pr]}{_ORD[od]}" if rc == "1" else ""
-        return f"fused group amaxes + grouped 1x16 quantize {_DT[dt]} {_RC[rc]}{err}"
+        return f"fused {kind} amaxes + 1x16 quantize {_DT[dt]} {_RC[rc]}{err}"
     m = re.match(r"void fos::k_colwise<(\d), (\d), (\d), (\d), (\d)>", name)
     if m:
         dt, rc, mt, pr, od = m.groups()
@@ -372,11 +615,15 @@ def describe_kernel(name: str) -> str:
         dt, gr = m.groups()
         return f"dequantize to {_DT[dt]} {_GR[gr]}"
     if "k_amax_tensor" in name:
-        return "amax per tensor (" + _DT.get(name.split("<")[1][0], "?") + ")"
+        return "amax per tensor"
+    if "k_amax_row" in name:
+        return "amax per row"
     if "k_zero_u32" in name:
         return "clear the amax word"
+    if "k_stream" in name:
+        return "streaming ceiling"
     if "copyBuffer" in name:
-        return "runtime copy (buffer set clones)"
+        return "runtime copy"
     return ""
 
 
@@ -391,270 +638,162 @@ def _counters(path):
     return {k: [v[d] for d in sorted(v)] for k, v in per.items()}
 
 
-def write_profiles(d):
-    """Write profiles/kernel_trace_bench_workloads.txt and the counter
-    summaries of the step's fused kernel and of the precomputed-amax quantize
-    kernel from the CSV files rocprofv3 wrote under d."""
+def _trace(path):
+    """{kernel: [(duration_ns, vgpr, lds_bytes, grid, workgroup)]} from a rocprofv3 kernel-trace CSV."""
     import csv
-    out_dir = os.path.join(ROOT, "profiles")
+    per = {}
+    for r in csv.DictReader(open(path)):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), int(r["VGPR_Count"]), int(r["LDS_Block_Size"]),
+             int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])))
+    return per
+
+
+def alg_blocks(stem: str) -> int:
+    """16-element blocks (units of quantizer work) one launch of the counter
+    workload `stem` processes, padding rows of the grouped tensor included."""
+    return {"quantize_grouped_bf16_65536x7168": (M5 + PAD5) * K5 // 16,
+            "quantize_16x16_bf16_4096x14336": 4096 * 14336 // 16,
+            "qdq_list_bf16_8x2048x7168": 8 * 2048 * 7168 // 16,
+            "fused_amax_quantize_bf16_8192x4096": _N2 // 16,
+            "quantize_1x16_bf16_8192x4096": _N2 // 16}[stem]
+
+
+def static_occupancy(vgpr: int, lds: int, wg: int) -> int:
+    """Waves per SIMD the registers and LDS allow (512 VGPRs per lane and
+    SIMD in granules of 8, at most 8 waves; 160 KiB of LDS per CU)."""
+    by_vgpr = min(8, 512 // max(8, -(-vgpr // 8) * 8))
+    waves_per_wg = max(1, wg // 64)
+    by_lds = 8 if lds == 0 else (160 * 1024 // lds) * waves_per_wg // 4
+    return max(0, min(by_vgpr, by_lds))
+
+
+def provenance(agent_csv=None):
+    """Provenance lines: the device (from rocprofv3's agent table when given,
+    else from torch), the software versions and the source hashes."""
+    import csv
+    import platform
+
+    import torch
+    lines = []
+    gpu = None
+    if agent_csv and os.path.exists(agent_csv):
+        gpu = next((r for r in csv.DictReader(open(agent_csv)) if r["Agent_Type"] == "GPU"), None)
+    if gpu:
+        lines += [f"gpu = {gpu['Name']} ({gpu['Vendor_Name']}), {gpu['Cu_Count']} CUs, {gpu['Simd_Count']} SIMDs, "
+                  f"{gpu['Num_Xcc']} XCDs, {gpu['Max_Waves_Per_Simd']} waves per SIMD, {gpu['Lds_Size_In_Kb']} KiB LDS "
+                  f"per CU, max engine clock {gpu['Max_Engine_Clk_Fcompute']} MHz"]
+    lines += [f"torch = {torch.__version__}", f"hip = {torch.version.hip}", f"python = {platform.python_version()}",
+              f"host_cores = {os.cpu_count()}", f"omp_num_threads = {os.environ.get('OMP_NUM_THREADS', '?')}",
+              f"kernel_source_sha256_16 = {kernel_source_hash()}",
+              f"bench_sha256_16 = {hashlib.sha256(open(os.path.abspath(__file__), 'rb').read()).hexdigest()[:16]}"]
+    return lines
+
+
+def write_profiles(d, out_dir=PROFILES):
+    """Write the kernel-trace summary of the step and the counter summary of
+    each kernel in COUNTER_KERNELS into out_dir from the CSV files rocprofv3
+    wrote under d."""
+    import synthdata
     os.makedirs(out_dir, exist_ok=True)
-    ksha = kernel_source_hash()
+    x, offs, _ = synthdata.grouped_tokens(M5, PAD5, K5, G5)
+    prov = provenance(os.path.join(d, "kt", "kt_agent_info.csv")) + [
+        f"input_sha256_grouped_bf16_{M5 + PAD5}x{K5} = {synthdata.sha256(x)}",
+                           f"input_sha256_grouped_offs = {hashlib.sha256(offs.tobytes()).hexdigest()}"]
+    del x
+    hdr = "# command (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):"
 
-    # kernel trace summary (rocprofv3 --stats)
-    stats = list(csv.DictReader(open(os.path.join(d, "kt", "kt_kernel_stats.csv"))))
-    lines = ["# rocprofv3 --kernel-trace --stats summary of the default bench (all workloads)",
-             "# command (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):",
-             "#   " + PROFILE_CMDS["kt"],
-             f"# kernel_source_sha256_16 = {ksha}",
-             "# durations in microseconds, per dispatch",
-             f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>6}  mode / kernel"]
-    avg = {}
-    for r in stats:
-        name = r["Name"]
-        avg[name] = float(r["AverageNs"]) / 1e3
+    # the step's kernel trace: every launch of the bench's default step (warmup included)
+    kt = _trace(os.path.join(d, "kt", "kt_kernel_trace.csv"))
+    durs = [t[0] for t in kt[HEADLINE_KERNEL]]
+    v, l, g, wg = kt[HEADLINE_KERNEL][0][1:]
+    lines = ["# rocprofv3 kernel trace of the bench's step: fos_quantize_grouped, bf16 65536 (+4096 padding) x 7168,",
+             "# 64 groups, four-over-six MSE exact, bound 448 (warmup and timed launches)", hdr,
+             "#   " + PROFILE_CMDS["kt"], "#   python3 $REPO/bench.py --write-profiles $OUT --profiles-out $REPO/profiles",
+             *prov, "# durations in microseconds, per dispatch",
+             f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel"]
+    for name, rows in sorted(kt.items(), key=lambda kv: -sum(r[0] for r in kv[1])):
+        ds = [r[0] / 1e3 for r in rows]
         desc = describe_kernel(name)
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
-                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):5.1f}%  "
-                     f"{desc + ' | ' if desc else ''}{name[:110]}")
-    if FUSED_KERNEL in avg:
-        lines.append(f"fused_kernel_avg_us = {avg[FUSED_KERNEL]:.2f}   # the bench step's one kernel")
-    if QUANT_KERNEL in avg:
-        lines.append(f"quantize_kernel_avg_us = {avg[QUANT_KERNEL]:.2f}   # bf16 8192x4096 quantize, precomputed amax")
-    open(os.path.join(out_dir, "kernel_trace_bench_workloads.txt"), "w").write("\n".join(lines) + "\n")
+        lines.append(f"{len(ds):6d} {sum(ds) / len(ds):9.2f} {min(ds):9.2f} {max(ds):9.2f}  "
+                     f"{desc + ' | ' if desc else ''}{name[:100]}")
+    lines += [f"headline_kernel = {HEADLINE_KERNEL}",
+              f"headline_kernel_calls = {len(durs)}",
+              f"headline_kernel_avg_us = {sum(durs) / len(durs) / 1e3:.2f}",
+              f"headline_kernel_median_us = {sorted(durs)[len(durs) // 2] / 1e3:.2f}",
+              f"vgpr_count = {v}", f"lds_bytes_per_workgroup = {l}", f"grid_threads = {g}", f"workgroup = {wg}",
+              f"static_occupancy_waves_per_simd = {static_occupancy(v, l, wg)}",
+              f"algorithmic_bytes_per_launch = {STEP_BYTES}",
+              f"achieved_GBs_at_avg = {STEP_BYTES / (sum(durs) / len(durs)) :.1f}"]
+    open(os.path.join(out_dir, os.path.basename(HEADLINE_TRACE)), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
-    # HBM counters, calibrated on a copy of known size
+    # per-workload kernel averages of the profile pass (each kernel below
+    # runs for one workload only there)
+    kp = _trace(os.path.join(d, "kt_pass", "kt_pass_kernel_trace.csv"))
     f = _counters(os.path.join(d, "fetch", "fetch_counter_collection.csv"))
     w = _counters(os.path.join(d, "write", "write_counter_collection.csv"))
-    sq_path = os.path.join(d, "sq", "sq_counter_collection.csv")
-    s = _counters(sq_path) if os.path.exists(sq_path) else None
+    s = _counters(os.path.join(d, "sq", "sq_counter_collection.csv"))
+    occ = _counters(os.path.join(d, "occ", "occ_counter_collection.csv"))
     copy_name = "__amd_rocclr_copyBuffer"
     cf = f[(copy_name, "FETCH_SIZE")][-4:]   # the profile pass ends with four copies of COPY_BYTES
     cw = w[(copy_name, "WRITE_SIZE")][-4:]
-    mean = lambda v: sum(v) / len(v)
+    mean = lambda vals: sum(vals) / len(vals)
     fetch_factor = COPY_BYTES / (mean(cf) * 1024)
     write_factor = COPY_BYTES / (mean(cw) * 1024)
-    n = _N
-    for kernel, (path, what, alg) in COUNTER_FILES.items():
-        qf = f[(kernel, "FETCH_SIZE")]
-        qw = w[(kernel, "WRITE_SIZE")]
-        rd = mean(qf) * 1024 * fetch_factor
-        wr = mean(qw) * 1024 * write_factor
-        lines = [f"# rocprofv3 counter summary: {what}; 1x16 blocks, bf16 8192x4096 N(0,1), four-over-six",
-                 "# MSE exact, E4M3 bound 448, per-tensor scale",
+    for kernel, (stem, what, alg) in COUNTER_KERNELS.items():
+        rows = kp[kernel]
+        us = mean([r[0] for r in rows]) / 1e3
+        v, l, g, wg = rows[0][1:]
+        rd = mean(f[(kernel, "FETCH_SIZE")]) * 1024 * fetch_factor
+        wr = mean(w[(kernel, "WRITE_SIZE")]) * 1024 * write_factor
+        get = lambda c: mean(s[(kernel, c)])
+        insts, cvt = get("SQ_INSTS_VALU"), get("SQ_INSTS_VALU_CVT")
+        # SQ_ACTIVE_INST_VALU counts quad-cycles (as rocprofv3's derived
+        # VALUBusy and OccupancyPercent take the SQ cycle counters)
+        valu_cyc = 4 * get("SQ_ACTIVE_INST_VALU") / N_SIMD
+        blocks = alg_blocks(stem)
+        occ_pct = mean(occ[(kernel, "OccupancyPercent")])
+        lines = [f"# rocprofv3 counter summary: {what}",
                  "# commands (after: cd /tmp && export TMPDIR=/tmp; OUT = an output folder, REPO = this repository):",
-                 "#   " + PROFILE_CMDS["fetch"], "#   " + PROFILE_CMDS["write"], "#   " + PROFILE_CMDS["sq"],
-                 "#   python3 $REPO/bench.py --write-profiles $OUT",
-                 "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch. The factors scale them to bytes so that the",
+                 *("#   " + PROFILE_CMDS[k] for k in ("kt_pass", "fetch", "write", "sq", "occ")),
+                 "#   python3 $REPO/bench.py --write-profiles $OUT --profiles-out $REPO/profiles",
+                 "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; the factors scale them to bytes so that the",
                  f"# profile pass's plain copy of {COPY_BYTES} bytes reads and writes exactly that many bytes.",
-                 f"kernel = {kernel}",
-                 f"kernel_source_sha256_16 = {ksha}",
-                 f"dispatches = {len(qf)}",
-                 f"fetch_size_kib = {mean(qf):.1f}",
-                 f"write_size_kib = {mean(qw):.1f}",
-                 f"copy_fetch_size_kib = {mean(cf):.1f}",
-                 f"copy_write_size_kib = {mean(cw):.1f}",
-                 f"fetch_factor = {fetch_factor:.4f}",
-                 f"write_factor = {write_factor:.4f}",
-                 f"hbm_read_bytes_per_launch = {rd:.0f}",
-                 f"hbm_write_bytes_per_launch = {wr:.0f}",
-                 f"hbm_bytes_per_launch = {rd + wr:.0f}",
-                 f"algorithmic_bytes_per_launch = {alg}",
-                 f"traffic_over_algorithmic = {(rd + wr) / alg:.4f}"]
-        if s is not None and (kernel, "SQ_INSTS_VALU") in s:
-            get = lambda c: mean(s[(kernel, c)])
-            valu = get("SQ_INSTS_VALU")
-            lines += [f"sq_waves = {get('SQ_WAVES'):.0f}",
-                      f"sq_insts_valu = {valu:.0f}   # wave instructions per dispatch",
-                      f"sq_insts_valu_cvt = {get('SQ_INSTS_VALU_CVT'):.0f}",
-                      f"sq_active_inst_valu = {get('SQ_ACTIVE_INST_VALU'):.0f}",
-                      f"sq_wave_cycles = {get('SQ_WAVE_CYCLES'):.0f}",
-                      f"sq_busy_cycles = {get('SQ_BUSY_CYCLES'):.0f}",
-                      f"sq_wait_inst_any = {get('SQ_WAIT_INST_ANY'):.0f}",
-                      f"grbm_gui_active = {get('GRBM_GUI_ACTIVE'):.0f}",
-                      f"valu_lane_insts_per_element = {valu * 64 / n:.2f}",
-                      f"valu_cvt_insts_per_block = {get('SQ_INSTS_VALU_CVT') * 64 / (n // 16):.2f}"]
+                 "# Each workload's buffers rotate over >= 1 GiB in the profile pass.",
+                 f"kernel = {kernel}", *prov,
+                 f"dispatches = {len(f[(kernel, 'FETCH_SIZE')])}",
+                 f"kernel_avg_us = {us:.2f}   # profile-pass kernel trace",
+                 f"achieved_GBs = {alg / (us * 1e3):.1f}",
+                 f"fetch_size_kib = {mean(f[(kernel, 'FETCH_SIZE')]):.1f}",
+                 f"write_size_kib = {mean(w[(kernel, 'WRITE_SIZE')]):.1f}",
+                 f"copy_fetch_size_kib = {mean(cf):.1f}", f"copy_write_size_kib = {mean(cw):.1f}",
+                 f"fetch_factor = {fetch_factor:.4f}", f"write_factor = {write_factor:.4f}",
+                 f"hbm_read_bytes_per_launch = {rd:.0f}", f"hbm_write_bytes_per_launch = {wr:.0f}",
+                 f"hbm_bytes_per_launch = {rd + wr:.0f}", f"algorithmic_bytes_per_launch = {alg}",
+                 f"traffic_over_algorithmic = {(rd + wr) / alg:.4f}",
+                 f"vgpr_count = {v}", f"lds_bytes_per_workgroup = {l}", f"grid_threads = {g}",
+                 f"static_occupancy_waves_per_simd = {static_occupancy(v, l, wg)}",
+                 f"occupancy_percent = {occ_pct:.1f}   # rocprofv3 OccupancyPercent (of 32 waves per CU)",
+                 f"occupancy_waves_per_simd = {occ_pct / 100 * 8:.2f}",
+                 f"valu_busy = {mean(occ[(kernel, 'VALUBusy')]) / 100:.4f}   # rocprofv3 VALUBusy",
+                 f"sq_waves = {get('SQ_WAVES'):.0f}",
+                 f"sq_insts_valu = {insts:.0f}   # wave instructions per dispatch",
+                 f"sq_insts_valu_cvt = {cvt:.0f}",
+                 f"sq_active_inst_valu = {get('SQ_ACTIVE_INST_VALU'):.0f}",
+                 f"sq_wave_cycles = {get('SQ_WAVE_CYCLES'):.0f}",
+                 f"sq_busy_cycles = {get('SQ_BUSY_CYCLES'):.0f}",
+                 f"sq_wait_inst_any = {get('SQ_WAIT_INST_ANY'):.0f}",
+                 f"grbm_gui_active = {get('GRBM_GUI_ACTIVE'):.0f}",
+                 f"wait_over_wave_cycles = {get('SQ_WAIT_INST_ANY') / max(1.0, get('SQ_WAVE_CYCLES')):.4f}",
+                 f"valu_cycles_per_simd = {valu_cyc:.0f}   # 4 x SQ_ACTIVE_INST_VALU / {N_SIMD} SIMDs",
+                 f"cycles_per_valu_inst = {4 * get('SQ_ACTIVE_INST_VALU') / insts:.2f}",
+                 f"valu_time_at_peak_clock_us = {valu_cyc / CLOCK_HZ * 1e6:.2f}   # at 2.4 GHz",
+                 f"valu_lane_insts_per_block = {insts * 64 / blocks:.1f}   # 16-element blocks the launch processes",
+                 f"valu_cvt_lane_insts_per_block = {cvt * 64 / blocks:.2f}"]
+        path = os.path.join(out_dir, f"counters_{stem}.txt")
         open(path, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
-
-
-def other_workloads(fos, synthdata, torch, np, c2, steps=50, warmup=5):
-    """Brief kernel-only timings of the other configurations (precomputed
-    amax); each figure is the median launch of its loop."""
-    out = {}
-
-    def gbs(nbytes, ms):
-        return round(nbytes / (ms * 1e-3) / 1e9, 1)
-
-    # the achievable ceiling in the same run: a plain 256 MiB device-to-device
-    # copy (reads and writes 256 MiB each), four buffer pairs in rotation
-    srcs = [torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    dsts = [torch.empty_like(t) for t in srcs]
-    _, ms = time_loop(lambda i: dsts[i].copy_(srcs[i]), len(srcs), 50, 5)
-    avg = float(np.median(ms))
-    out["copy_256MiB_device_to_device"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(2 * COPY_BYTES, avg),
-                                           "frac": round(gbs(2 * COPY_BYTES, avg) / PEAK_HBM_GBS, 4)}
-    log(f"[bench] device copy 256 MiB: {avg * 1e3:.1f} us, {gbs(2 * COPY_BYTES, avg):.0f} GB/s (the ceiling)")
-    del srcs, dsts
-
-    # the dense activation tensor: the quantize kernel alone with a
-    # precomputed amax (the pages' kernel metric), and the two-launch step
-    xs, codes, scales, amax, sdec, knobs = c2
-    n = xs[0].numel()
-    qb = n * 2 + n // 2 + n // 16
-    for i in range(len(xs)):
-        fos.fos_amax(xs[i], "tensor", out=amax[i])
-    _, ms = time_loop(lambda i: fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i],
-                                                 **knobs), len(xs), 200, 10)
-    avg = float(np.median(ms))
-    out["quantize_1x16_bf16_8192x4096_precomputed_amax"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
-                                                            "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
-    log(f"[bench] quantize bf16 8192x4096, precomputed amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
-
-    # the same tensor with per-row global scales (one amax per row)
-    row_amax = [fos.fos_amax(xs[i], "row") for i in range(len(xs))]
-    rknobs = dict(knobs, scale_gran="row")
-    rsdec = torch.empty(xs[0].shape[0], dtype=torch.float32, device="cuda")
-    _, ms = time_loop(lambda i: fos.fos_quantize(xs[i], row_amax[i], codes=codes[i], scales=scales[i], sdec=rsdec,
-                                                 **rknobs), len(xs), 200, 10)
-    avg = float(np.median(ms))
-    out["quantize_1x16_bf16_8192x4096_per_row_amax"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
-                                                        "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
-    log(f"[bench] quantize bf16 8192x4096, per-row amax: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
-    # per-row amaxes computed on the device: one launch (each row read from
-    # HBM once), against fos_amax per row followed by fos_quantize
-    ra = torch.empty(xs[0].shape[0], dtype=torch.float32, device="cuda")
-    for key, fn in (("fused_row_amax_quantize_bf16_8192x4096",
-                     lambda i: fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=ra, sdec=rsdec,
-                                                      **rknobs)),
-                    ("row_amax_then_quantize_bf16_8192x4096",
-                     lambda i: (fos.fos_amax(xs[i], "row", out=ra),
-                                fos.fos_quantize(xs[i], ra, codes=codes[i], scales=scales[i], sdec=rsdec, **rknobs)))):
-        _, ms = time_loop(fn, len(xs), 200, 10)
-        avg = float(np.median(ms))
-        out[key] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg), "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
-        log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s (x read once + codes and scales)")
-    del row_amax, ra
-
-    # fused fake quantization of the same tensor with its amax computed on
-    # the device: one launch that reads x once, against fos_amax + fos_qdq
-    ys2 = [torch.empty_like(x) for x in xs]
-    qkw = dict(recipe="4over6", err_metric="mse", err_prec="fp16", bound=448)
-    qws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
-    qb2 = n * 2 + n * 2
-    for key, fn in (("qdq_fused_amax_bf16_8192x4096_4over6_mse_fp16_448",
-                     lambda i: fos.fos_qdq_fused(xs[i], out=ys2[i], amax=amax[i], workspace=qws, **qkw)),
-                    ("amax_then_qdq_bf16_8192x4096_4over6_mse_fp16_448",
-                     lambda i: (fos.fos_amax(xs[i], "tensor", out=amax[i]),
-                                fos.fos_qdq(xs[i], amax[i], out=ys2[i], **qkw)))):
-        _, ms = time_loop(fn, len(xs), 200, 10)
-        avg = float(np.median(ms))
-        out[key] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb2, avg), "frac": round(gbs(qb2, avg) / PEAK_HBM_GBS, 4)}
-        log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(qb2, avg):.0f} GB/s (x read once, y written)")
-    del ys2
-
-    def two_launches(i):
-        fos.fos_amax(xs[i], "tensor", out=amax[i])
-        fos.fos_quantize(xs[i], amax[i], codes=codes[i], scales=scales[i], sdec=sdec[i], **knobs)
-    _, ms = time_loop(two_launches, len(xs), 200, 10)
-    avg = float(np.median(ms))
-    out["amax_then_quantize_bf16_8192x4096"] = {"avg_step_us": round(avg * 1e3, 2), "GB/s": gbs(qb + 2 * n, avg)}
-    log(f"[bench] fos_amax + fos_quantize (two launches): {avg * 1e3:.1f} us")
-
-    # columnwise quantize (the transpose's codes and scales) of the same tensor
-    ct = torch.empty(xs[0].shape[1], xs[0].shape[0] // 2, dtype=torch.uint8, device="cuda")
-    st = torch.empty(xs[0].shape[1], xs[0].shape[0] // 16, dtype=torch.uint8, device="cuda")
-    _, ms = time_loop(lambda i: fos.fos_quantize_columnwise(xs[i], amax[i], codes=ct, scales=st, sdec=sdec[i],
-                                                            **knobs), len(xs), 200, 10)
-    avg = float(np.median(ms))
-    out["quantize_columnwise_bf16_8192x4096"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
-                                                 "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
-    log(f"[bench] columnwise bf16 8192x4096: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
-    del ct, st
-
-    # nvfp4_dequantize of the step's outputs back to bf16 (the dequantized-
-    # backward recompute): reads 0.5625 B/elem, writes 2 B/elem
-    ys = [torch.empty_like(x) for x in xs]
-    _, ms = time_loop(lambda i: fos.nvfp4_dequantize(codes[i], scales[i], sdec[i], "tensor", torch.bfloat16,
-                                                     out=ys[i]), len(xs), 200, 10)
-    avg = float(np.median(ms))
-    out["dequantize_bf16_8192x4096"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(qb, avg),
-                                        "frac": round(gbs(qb, avg) / PEAK_HBM_GBS, 4)}
-    log(f"[bench] dequantize bf16 8192x4096: {avg * 1e3:.1f} us, {gbs(qb, avg):.0f} GB/s")
-    del ys
-
-    # 16x16 weights, bf16 4096x14336 and fp32 4096x4096, per-tensor, MSE exact, 448
-    for dtype, (M, K) in (("bf16", (4096, 14336)), ("fp32", (4096, 4096))):
-        w = synthdata.weight(M, K, 31, dtype).to("cuda")
-        a = fos.fos_amax(w, "tensor")
-        eb = 2 if dtype == "bf16" else 4
-        nbytes = M * K * eb + M * K // 2 + M * K // 16
-        ws = rotating(w, nbytes)
-        c = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
-        s = torch.empty(M, K // 16, dtype=torch.uint8, device="cuda")
-        sd = torch.empty(1, dtype=torch.float32, device="cuda")
-        _, ms = time_loop(lambda i: fos.fos_quantize(ws[i], a, codes=c, scales=s, sdec=sd, recipe="4over6",
-                                                     block="16x16", err_metric="mse", err_prec="exact"),
-                          len(ws), steps, warmup)
-        avg = float(np.median(ms))
-        out[f"quantize_16x16_{dtype}_{M}x{K}"] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
-                                                  "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
-        log(f"[bench] 16x16 {dtype} {M}x{K}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
-        del ws, w
-
-    # fused QDQ over 8 expert weights 2048x7168, bf16 and fp16, the five timed modes
-    lst = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=("bf16", "fp16"))
-    for dtype in ("bf16", "fp16"):
-        xs = [t.to("cuda") for t in lst[dtype]]
-        ams = [fos.fos_amax(t, "tensor") for t in xs]
-        ys = [torch.empty_like(t) for t in xs]
-        nbytes = sum(t.numel() for t in xs) * 4
-        for mode in (("nvfp4", "mse", "fp16", 448), ("4over6", "mae", "fp16", 448), ("4over6", "mae", "fp16", 256),
-                     ("4over6", "mse", "fp16", 448), ("4over6", "mse", "fp16", 256)):
-            r, m, p, bnd = mode
-            _, ms = time_loop(lambda i: fos.fos_qdq_list(xs, ams, outs=ys, recipe=r, err_metric=m, err_prec=p,
-                                                         bound=bnd), 1, steps, warmup)
-            avg = float(np.median(ms))
-            key = f"qdq_list_8x2048x7168_{dtype}_{r}" + ("" if r == "nvfp4" else f"_{m}_{p}_{bnd}")
-            out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
-                        "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
-            log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
-        del xs, ys
-    del lst
-
-    # grouped MoE activations: 65536 (+4096 padding) x 7168, 64 groups, MSE exact
-    M, pad, K, G = 65536, 4096, 7168, 64
-    x, offs, fac = synthdata.grouped_tokens(M, pad, K, G)
-    x = x.to("cuda")
-    offs_d = torch.from_numpy(offs).to("cuda")
-    starts = np.concatenate([[0], offs[:-1]])
-    gam = torch.stack([fos.fos_amax(x[s:e].contiguous(), "tensor")[0] if e > s else
-                       torch.zeros((), device="cuda") for s, e in zip(starts, offs)])
-    c = torch.empty(M + pad, K // 2, dtype=torch.uint8, device="cuda")
-    s = torch.empty(M + pad, K // 16, dtype=torch.uint8, device="cuda")
-    nbytes = M * K * 2 + (M + pad) * (K // 2 + K // 16)
-    for bnd in (448, 256):
-        _, ms = time_loop(lambda i: fos.fos_quantize_grouped(x, offs_d, gam, codes=c, scales=s, recipe="4over6",
-                                                             err_metric="mse", err_prec="exact", bound=bnd),
-                          1, steps, warmup)
-        avg = float(np.median(ms))
-        key = f"quantize_grouped_{M}+{pad}x{K}_G{G}_{bnd}"
-        out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(nbytes, avg),
-                    "frac": round(gbs(nbytes, avg) / PEAK_HBM_GBS, 4)}
-        log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(nbytes, avg):.0f} GB/s")
-    # the group amaxes and the grouped quantize in one launch: x's data rows
-    # are read twice (amax phase, quantize phase)
-    ga = torch.empty(G, dtype=torch.float32, device="cuda")
-    gs = torch.empty(G, dtype=torch.float32, device="cuda")
-    fbytes = nbytes + M * K * 2
-    _, ms = time_loop(lambda i: fos.fos_quantize_grouped_fused(x, offs_d, codes=c, scales=s, group_amax=ga,
-                                                               group_sdec=gs, recipe="4over6", err_metric="mse",
-                                                               err_prec="exact", bound=448), 1, steps, warmup)
-    avg = float(np.median(ms))
-    key = f"fused_amax_quantize_grouped_{M}+{pad}x{K}_G{G}_448"
-    out[key] = {"avg_launch_us": round(avg * 1e3, 2), "GB/s": gbs(fbytes, avg),
-                "frac": round(gbs(fbytes, avg) / PEAK_HBM_GBS, 4)}
-    log(f"[bench] {key}: {avg * 1e3:.1f} us, {gbs(fbytes, avg):.0f} GB/s")
-    return out
 
 
 if __name__ == "__main__":

@@ -1,5 +1,6 @@
 """Host logic of bench.py (CPU only): the one-GPU contract, the profile
-summaries' freshness rule, the kernel descriptions and the step's bytes."""
+summaries' freshness rule, the kernel descriptions, the step's bytes and the
+static occupancy rule."""
 import os
 import subprocess
 import sys
@@ -37,7 +38,9 @@ def test_kernel_descriptions():
         "1x16 quantize bf16 4over6 mse exact tensor"
     assert d("void fos::k_1x16<48, 1, 1, 0, 1, 1, 0, 1>(fos::Args1x16<48>)") == \
         "1x16 qdq list<48> fp16 4over6 mae fp16err seq tensor"
-    assert d(bench.FUSED_KERNEL) == "fused amax + 1x16 quantize (one read) bf16 4over6 mse exact tensor"
+    assert d("void fos::k_fused_onchip<0, 1, 1, 0, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)") == \
+        "fused amax + 1x16 quantize (one read) bf16 4over6 mse exact tensor"
+    assert d(bench.HEADLINE_KERNEL) == "1x16 quantize bf16 4over6 mse exact grouped"
     assert d("void fos::k_fused_onchip<1, 1, 0, 1, 0, 1>(fos::Args1x16<1>, unsigned int*, float*)") == \
         "fused amax + 1x16 qdq (one read) fp16 4over6 mae fp16err tensor"
     assert d("void fos::k_fused<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)") == \
@@ -45,17 +48,29 @@ def test_kernel_descriptions():
     assert d("void fos::k_16x16<2, 1, 1, 0, 1, 0>(fos::Args16x16)").startswith("16x16 quantize fp32 4over6")
     assert "grouped" in d("void fos::k_fused_grouped<0, 1, 1, 0, 0>(fos::Args1x16<1>, unsigned int*, float*)")
     assert d("void fos::k_fused_row<0, 1, 1, 0, 0>(fos::Args1x16<1>, float*)") == \
-        "fused per-row amaxes + 1x16 quantize bf16 4over6 mse exact row"
+        "fused row amaxes + 1x16 quantize bf16 4over6 mse exact"
     assert d("void fos::k_colwise<0, 1, 1, 0, 0>(fos::Args16x16)").startswith("columnwise")
     assert d("void fos::k_dequant<0, 0>(unsigned char const*)") == "dequantize to bf16 tensor"
     assert d("some_other_kernel") == ""
 
 
-def test_step_bytes_of_the_dense_activation_step():
-    # per 1x16 block: one read of 32 B (the amax and the quantize share it,
-    # the tensor staying on chip in between) + codes 8 B + scale 1 B
-    M, K = 8192, 4096
-    blocks = M * K // 16
-    assert blocks * 41 == 85983232
-    assert bench.COUNTER_FILES[bench.FUSED_KERNEL][2] == 85983232
-    assert bench.COUNTER_FILES[bench.QUANT_KERNEL][2] == blocks * 41
+def test_step_bytes_of_the_grouped_step():
+    # the 65536 data rows are read once (2 B per element); codes and scales
+    # are written for all 69632 rows, padding included (0.5625 B per element)
+    M, pad, K = 65536, 4096, 7168
+    assert bench.STEP_BYTES == M * K * 2 + (M + pad) * K * 9 // 16 == 1220280320
+    assert bench.COUNTER_KERNELS[bench.HEADLINE_KERNEL][2] == bench.STEP_BYTES
+    # per 1x16 block of the dense activation tensor: 32 B read, codes 8 B, scale 1 B
+    blocks = 8192 * 4096 // 16
+    for name, (_, _, alg) in bench.COUNTER_KERNELS.items():
+        if "8192x4096" in bench.COUNTER_KERNELS[name][0]:
+            assert alg == blocks * 41
+
+
+def test_static_occupancy():
+    occ = bench.static_occupancy
+    assert occ(64, 0, 256) == 8
+    assert occ(87, 0, 256) == 5      # 88 VGPRs: 512 // 88
+    assert occ(128, 0, 256) == 4
+    assert occ(87, 36864, 256) == 4  # 4 workgroups of 36 KiB per CU: 16 waves
+    assert occ(200, 0, 256) == 2
