@@ -475,6 +475,8 @@ def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
     # fused QDQ over the 8 expert weights 2048x7168, bf16 and fp16, the five
     # timed modes, each list rotated over >= 1 GiB (3 copies)
     lst = synthdata.expert_weight_list(8, 2048, 7168, 40, dtypes=("bf16", "fp16"))
+    lws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    lst_status = torch.zeros(1, dtype=torch.int32, device="cuda")
     for dtype in ("bf16", "fp16"):
         base = [t.to("cuda") for t in lst[dtype]]
         nbytes = sum(t.numel() for t in base) * 4
@@ -491,7 +493,18 @@ def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
             key = f"qdq_list_8x2048x7168_{dtype}_{r}" + ("" if r == "nvfp4" else f"_{m}_{p}_{bnd}")
             out[key] = entry(nbytes, ms, rotating_sets=nsets)
             log(f"[bench] {key}: {out[key]['avg_launch_us']} us, {out[key]['GB/s']} GB/s")
+            # the same list with every weight's amax computed in the launch
+            # (the end-to-end step of the fake-quantization loop)
+            fa = [torch.empty(8, dtype=torch.float32, device="cuda") for _ in range(nsets)]
+            ms = float(np.median(time_loop(lambda i: fos.fos_qdq_list_fused(sets[i], outs=ys[i], amax=fa[i], recipe=r,
+                                                                            err_metric=m, err_prec=p, bound=bnd,
+                                                                            workspace=lws, status=lst_status),
+                                           nsets, steps, warmup)))
+            out["fused_amax_" + key] = entry(nbytes, ms, rotating_sets=nsets,
+                                             note="one launch: every amax, then the QDQ; x read twice")
+            log(f"[bench] fused_amax_{key}: {ms * 1e3:.2f} us, {gbs(nbytes, ms)} GB/s")
         del sets, ys, ams, base
+    out["fused_calls_status_clean"] = int(lst_status.item()) == 0 and int(st.item()) == 0
     return out
 
 

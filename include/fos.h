@@ -279,6 +279,25 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
 int fos_qdq_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_config* cfg, void* y, float* amax_out,
                   void* workspace, int32_t* d_status, void* stream);
 
+/* Every tensor's amax and fos_qdq_list in one launch (added in ABI version
+ * 5): the Megatron-LM PR's fake-quantization loop computes one FP32 amax per
+ * weight before its fused data path ("What does this PR do?"; its
+ * "Performance" section times that amax as part of the fused primary); here
+ * the amaxes come from the first phase of the list launch itself. The
+ * result equals fos_amax(..., FOS_AMAX_TENSOR) of each tensor followed by
+ * fos_qdq_list with those amaxes, bit for bit. cfg must be 1x16 with
+ * FOS_PER_TENSOR; each descs[i].amax is ignored (may be NULL).
+ *   amax_out:  device float[n] (not NULL): amax_out[i] receives tensor i's
+ *              NaN-dropping max |x| (+0 for a tensor with no elements).
+ *   workspace, d_status: as for fos_quantize_fused. The call shares the
+ *              grouped fused call's slots and call counter, so the two may
+ *              use one workspace one after the other.
+ * One launch takes up to 48 tensors (longer lists take one launch per 48).
+ * The launch reads every input twice (amax phase, QDQ phase); the second
+ * read comes from the Infinity Cache when the list fits there (256 MB). */
+int fos_qdq_list_fused(int n, const fos_tensor_desc* descs, int dtype, const fos_config* cfg, float* amax_out,
+                       void* workspace, int32_t* d_status, void* stream);
+
 /* Grouped (MoE) amax and quantize in one launch: the group amaxes that
  * fos_quantize_grouped takes as input (pytorch/ao PR, MoE commit; the
  * Megatron-LM PR's separate amax pre-pass, "What does this PR do?") are

@@ -63,6 +63,7 @@ _SIGS = {
     "fos_quantize": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_qdq": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P]),
     "fos_qdq_list": (_I, [_I, _P, _I, ctypes.POINTER(_Config), _P]),
+    "fos_qdq_list_fused": (_I, [_I, _P, _I, ctypes.POINTER(_Config), _P, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _I64, _I64, _P, _I, _I, _P, _P]),
     "fos_quantize_grouped": (_I, [_P, _I, _I64, _I64, _P, _I, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_quantize_fused": (_I, [_P, _I, _I64, _I64, ctypes.POINTER(_Config), _P, _P, _P, _P, _P, _P, _P]),
@@ -340,6 +341,37 @@ def fos_qdq_list(xs: Sequence[torch.Tensor], amaxes: Sequence[torch.Tensor], *, 
         _check(load_library().fos_qdq_list(len(xs), ctypes.cast(descs, ctypes.c_void_p), DTYPES[xs[0].dtype],
                                            ctypes.byref(cfg), _stream(dev)))
     return ys
+
+
+def fos_qdq_list_fused(xs: Sequence[torch.Tensor], *, outs=None, amax=None, workspace=None, status=None,
+                       check=False, **knobs):
+    """Every tensor's amax and the fused quantize-dequantize of the list in one
+    launch. Returns (ys, amax float32[n]). `workspace`, `status` and `check`
+    as for fos_quantize_fused."""
+    if not xs:
+        return [], None
+    dev = xs[0].device
+    ys = [torch.empty_like(x) for x in xs] if outs is None else list(outs)
+    if amax is None:
+        amax = torch.empty(len(xs), dtype=torch.float32, device=dev)
+    descs = (_Desc * len(xs))()
+    for i, (x, y) in enumerate(zip(xs, ys)):
+        _need(x, f"xs[{i}]")
+        if x.dtype != xs[0].dtype or x.device != dev:
+            raise ValueError("all tensors of a list share one dtype and device")
+        descs[i] = _Desc(x.data_ptr(), y.data_ptr(), None, x.shape[0], x.shape[1])
+    cfg = config(**knobs)
+    if workspace is None:
+        workspace = fused_workspace(dev)
+    own = status is None
+    if own:
+        status = fused_status_word(dev)
+    with torch.cuda.device(dev):
+        _check(load_library().fos_qdq_list_fused(len(xs), ctypes.cast(descs, ctypes.c_void_p), DTYPES[xs[0].dtype],
+                                                 ctypes.byref(cfg), _ptr(amax), _ptr(workspace), _ptr(status),
+                                                 _stream(dev)))
+    _fused_done(dev, status, own, check)
+    return ys, amax
 
 
 def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, sdec: torch.Tensor, scale_gran: str = "tensor",

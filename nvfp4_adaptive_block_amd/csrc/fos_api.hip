@@ -323,6 +323,56 @@ int fos_qdq_list(int n, const fos_tensor_desc* descs, int dtype, const fos_confi
   return FOS_OK;
 }
 
+int fos_qdq_list_fused(int n, const fos_tensor_desc* descs, int dtype, const fos_config* cfg, float* amax_out,
+                       void* workspace, int32_t* d_status, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (cfg->block != FOS_BLOCK_1X16 || cfg->scale_gran != FOS_PER_TENSOR)
+    return fail(FOS_ERR_CONFIG, "fused amaxes + QDQ list supports 1x16 blocks with a per-tensor scale");
+  if (n < 0) return fail(FOS_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !descs) return fail(FOS_ERR_INVALID_ARG, "descs is NULL");
+  if (n > 0 && !amax_out) return fail(FOS_ERR_INVALID_ARG, "amax_out must be non-NULL");
+  if (!workspace) return fail(FOS_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (!aligned(amax_out, 4) || !aligned(workspace, 8) || !aligned(d_status, 4))
+    return fail(FOS_ERR_ALIGN, "amax_out/workspace/status misaligned");
+  for (int i = 0; i < n; i++) {
+    const fos_tensor_desc& d = descs[i];
+    if ((rc = check_shape(d.M, d.K, FOS_BLOCK_1X16))) return fail(rc, "tensor %d: %s", i, g_last_error.c_str());
+    if (d.M * d.K > 0 && (!d.x || !d.y)) return fail(FOS_ERR_INVALID_ARG, "tensor %d: x/y is NULL", i);
+    if (!aligned(d.x, 16) || !aligned(d.y, 16)) return fail(FOS_ERR_ALIGN, "tensor %d: x/y not 16-byte aligned", i);
+  }
+  if ((rc = check_device())) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int metric, prec, order;
+  mode_of(cfg, metric, prec, order);
+  const int64_t ub = fos::unit_blocks(fos::kOutQdq, dtype);
+  int i = 0;
+  while (i < n) {
+    fos::Args1x16<fos::kMaxList> a;
+    memset(&a, 0, sizeof a);
+    int64_t units = 0;
+    for (; i < n && a.n < fos::kMaxList; i++) {
+      const fos_tensor_desc& d = descs[i];
+      if (d.M * d.K == 0) {  // no elements: the amax is +0
+        if ((rc = launch_status(fos::launch_zero_u32(amax_out + i, 1, s)))) return rc;
+        continue;
+      }
+      a.t[a.n++] = fos::TensorRef{d.x, d.y, nullptr, d.M, d.K, units, amax_out + i};
+      units += (d.M * (d.K / 16) + ub - 1) / ub;  // 64 blocks of the flattened tensor
+    }
+    if (a.n == 0) continue;
+    a.total_units = units;
+    a.six_b = six_b(cfg);
+    a.status = d_status;
+    a.spin_limit = g_poll_limit.load(std::memory_order_relaxed);
+    if ((rc = launch_status(fos::launch_fused_list(dtype, cfg->recipe, metric, prec, order, a,
+                                                   static_cast<uint32_t*>(workspace), s))))
+      return rc;
+  }
+  return FOS_OK;
+}
+
 int fos_qdq(const void* x, int dtype, int64_t M, int64_t K, const float* amax, const fos_config* cfg, void* y,
             void* stream) {
   fos_tensor_desc d{x, y, amax, M, K};

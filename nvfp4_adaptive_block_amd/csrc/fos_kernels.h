@@ -59,6 +59,7 @@ struct TensorRef {
   const float* amax;
   int64_t M, K;
   int64_t unit_begin;
+  float* amax_out;  // fused list: receives the tensor's amax (nullable)
 };
 
 template <int NT>
@@ -101,6 +102,8 @@ hipError_t launch_fused_grouped(int dt, int recipe, int metric, int prec, int or
                                 uint32_t* ws, float* amax_out, hipStream_t s);
 hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, int gran,
                            const Args1x16<kMaxList>& a, hipStream_t s);
+hipError_t launch_fused_list(int dt, int recipe, int metric, int prec, int order, const Args1x16<kMaxList>& a,
+                             uint32_t* ws, hipStream_t s);
 hipError_t launch_colwise(int dt, int recipe, int metric, int prec, int order, const Args16x16& a, hipStream_t s);
 hipError_t launch_16x16(int dt, int recipe, int metric, int prec, int gran, int out, const Args16x16& a,
                         hipStream_t s);

@@ -522,10 +522,21 @@ __device__ __forceinline__ void unit_1x16(const Raw<DT>* raw, float S_enc, float
   }
 }
 
+// Zero codes and scales for the lane's blocks of a quantize unit.
+template <int DT>
+__device__ __forceinline__ void zero_unit_1x16(const Unit& U, int lane) {
+  constexpr int kNB = unit_blocks(kOutQuant, DT) / 64;
+#pragma unroll
+  for (int j = 0; j < kNB; j++) {
+    store_codes(U.out, lane * 8 + j * 64 * 8, 0u, 0u);
+    store_scale(U.scl, lane + j * 64, 0u);
+  }
+}
+
 // The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED the
 // amaxes come from `fused_amax` (LDS, as float bits) rather than from
-// memory: [1] for a per-tensor scale, [G] for grouped scales, and for
-// per-row scales [1], the amax of the one row the range covers.
+// memory: per-tensor scales [n], one per tensor of the launch; grouped
+// scales [G]; per-row scales [1], the amax of the one row the range covers.
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT, bool FUSED>
 __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
                                           int64_t u_end, const uint32_t* fused_amax) {
@@ -546,7 +557,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
 
     float S_enc = 1.0f, S_dec = 1.0f;
     if (GRAN == kGranTensor) {
-      S_enc = global_encode_scale(FUSED ? __uint_as_float(fused_amax[0]) : ld_const(T.amax, 0), six_b);
+      S_enc = global_encode_scale(FUSED ? __uint_as_float(fused_amax[ti]) : ld_const(T.amax, 0), six_b);
       S_dec = 1.0f / S_enc;
       tab.build(S_enc, S_dec, lane);
     }
@@ -562,6 +573,14 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
     // (two stores). Units past the range compute on zeros and their stores
     // fall outside their resources.
     auto process = [&](const Raw<DT>* raw, const UPos& pos, bool valid, const Unit& U) {
+      if (GRAN == kGranGroup && pos.row >= rows_read) {
+        // a padding unit (wave-uniform: group offsets are multiples of 16
+        // rows, so a flat unit never straddles offs[G-1], and a per-row unit
+        // lies in one row): its outputs are zero, which is what quantizing
+        // its zeros would give, so nothing is computed
+        zero_unit_1x16<DT>(U, lane);
+        return;
+      }
       if (GRAN != kGranTensor) {
         const int64_t row = pos.row;  // wave-uniform
         if (valid && row != tab_row) {
@@ -623,6 +642,28 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
   }
 }
 
+// The wave's share [u, u_end) of units [begin, end): contiguous ranges of
+// equal size, in wave order.
+__device__ __forceinline__ void wave_range(int64_t begin, int64_t end, int64_t wave, int64_t nwaves, int64_t& u,
+                                           int64_t& u_end) {
+  const int64_t per = (end - begin + nwaves - 1) / nwaves;
+  u = min(end, begin + wave * per);
+  u_end = min(end, u + per);
+}
+
+// Units of a grouped launch that hold data rows (rows before offs[G-1]);
+// the units after them are padding. Group offsets are multiples of 16 rows,
+// so with flat units the boundary falls between two units.
+template <int DT, int NT>
+__device__ __forceinline__ int64_t grouped_data_units(const Args1x16<NT>& args) {
+  constexpr int64_t kUB = unit_blocks(kOutQuant, DT);
+  const TensorRef& T = args.t[0];
+  const int64_t rows = min(max((int64_t)ld_const(args.offs, args.G - 1), (int64_t)0), T.M);
+  const int64_t nbk = T.K >> 4;
+  const int64_t d = grouped_flat(T.K, kUB) ? (rows * nbk + kUB - 1) / kUB : rows * ((nbk + kUB - 1) / kUB);
+  return min(d, args.total_units);
+}
+
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
   __shared__ float lds[4][256];
@@ -634,11 +675,18 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
 
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
-  const int64_t u = wave * per;
-  const int64_t u_end = min(args.total_units, u + per);
-  if (u >= u_end) return;
-  walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr);
+  int64_t u, u_end;
+  if (GRAN == kGranGroup) {
+    // the data units, then the padding units (zero outputs, nothing
+    // computed), each dealt out evenly, so that no wave holds only padding
+    const int64_t D = grouped_data_units<DT>(args);
+    wave_range(0, D, wave, nwaves, u, u_end);
+    if (u < u_end) walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr);
+    wave_range(D, args.total_units, wave, nwaves, u, u_end);
+  } else {
+    wave_range(0, args.total_units, wave, nwaves, u, u_end);
+  }
+  if (u < u_end) walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr);
 }
 
 // NaN-dropping magnitude max over packed 16-bit pairs: with m = |h| bits,
@@ -1738,9 +1786,11 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
   const int G = args.G;
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
-  const int64_t u = min(args.total_units, wave * per);
-  const int64_t u_end = min(args.total_units, u + per);
+  // the data units, then the padding units, each dealt out evenly (phase 1
+  // reads only data rows; phase 2 writes zeros for the padding units)
+  const int64_t D = grouped_data_units<DT>(args);
+  int64_t u, u_end;
+  wave_range(0, D, wave, nwaves, u, u_end);
   const TensorRef& T = args.t[0];
   const int64_t nbk = T.K >> 4, spr = (nbk + kUB - 1) / kUB;
   const bool flat = grouped_flat(T.K, kUB);
@@ -1814,8 +1864,92 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
   }
 
   // phase 2
+  if (u < u_end) walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, u_end, gm);
+  wave_range(D, args.total_units, wave, nwaves, u, u_end);
+  if (u < u_end) walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, u_end, gm);
+}
+
+// ------------------------------------------------------------ fused amaxes + QDQ list
+
+// Every tensor's amax and the fused QDQ of a list of tensors in one launch:
+// the per-weight FP32 amax pre-pass of the Megatron-LM page's fake-
+// quantization loop ("What does this PR do?", "Performance": the fused
+// primary includes one amax per weight) folded into the list launch. Phase
+// 1: each wave takes the NaN-dropping max |x| over the part of its unit
+// range in each tensor it touches; the workgroup combines its waves' maxima
+// per tensor in LDS and adds them to the workspace's slots (banked as for
+// the grouped kernel, whose slots and call counter it shares). After the
+// grid barrier, phase 2 is the list walk of the QDQ with the tensor amaxes
+// held in LDS; it reads the inputs a second time, from the Infinity Cache
+// when the list fits there.
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER>
+__global__ void __launch_bounds__(256) k_fused_list(const Args1x16<kMaxList> args, uint32_t* workspace) {
+  constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
+  constexpr int kR = __ATOMIC_RELAXED;
+  constexpr int kUB = unit_blocks(kOutQdq, DT);
+  __shared__ float lds[4][256];
+  __shared__ uint32_t gm[kMaxList];
+  __shared__ uint32_t gen0, bank;
+  __shared__ int ok;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const Table tab{lds[wv], lds[wv] + 128};
+  const BarWs ws{workspace};
+  const int n = args.n;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
+  const int64_t u = min(args.total_units, wave * per);
+  const int64_t u_end = min(args.total_units, u + per);
+
+  for (int t = threadIdx.x; t < n; t += blockDim.x) gm[t] = 0u;
+  if (threadIdx.x == 0) {
+    gen0 = barrier_generation(ws);
+    bank = __hip_atomic_load(ws.ggen(), kR, kA) & 1u;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)  // every slot: the next banked call may have more groups or tensors
+    for (int g = threadIdx.x; g < kMaxFusedGroups; g += blockDim.x) __hip_atomic_store(ws.gslot(bank ^ 1u, g), 0u, kR, kA);
+
+  // phase 1: the wave's units [u, u_end) intersected with each tensor's
+  // units; a tensor's units are 64 consecutive blocks of its flattened data
+  if (u < u_end) {
+    int ti = 0;
+    while (ti + 1 < n && args.t[ti + 1].unit_begin <= u) ti++;
+    for (; ti < n; ti++) {
+      const TensorRef& T = args.t[ti];
+      const int64_t tb = T.unit_begin;
+      const int64_t te = (ti + 1 < n) ? args.t[ti + 1].unit_begin : args.total_units;
+      const int64_t lo = max(u, tb), hi = min(u_end, te);
+      if (lo < hi) {
+        const int64_t nblk = T.M * (T.K >> 4);
+        const uint32_t m = wave_max_u32(range_absmax<DT>(T.x, (lo - tb) * kUB, min(nblk, (hi - tb) * kUB), lane));
+        if (lane == 0 && m) atomicMax(&gm[ti], m);
+      }
+      if (te >= u_end) break;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += blockDim.x)
+    if (gm[t]) __hip_atomic_fetch_max(ws.gslot(bank, t), gm[t], kR, kA);
+  vm_wait();  // this wave's additions are done before the workgroup arrives
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t unused = 0;
+    ok = grid_max_barrier(ws, gen0, 0u, unused, ws.ggen(), args.spin_limit) ? 1 : 0;
+    if (!ok && args.status) atomicOr(args.status, kStatusBarrier);
+  }
+  __syncthreads();
+  if (!ok) return;
+  for (int t = threadIdx.x; t < n; t += blockDim.x) gm[t] = __hip_atomic_load(ws.gslot(bank, t), kR, kA);
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int t = threadIdx.x; t < n; t += blockDim.x)
+      if (args.t[t].amax_out) args.t[t].amax_out[0] = __uint_as_float(gm[t]);
+
+  // phase 2
   if (u >= u_end) return;
-  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, u_end, gm);
+  walk_1x16<kMaxList, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQdq, true>(args, tab, lane, u, u_end, gm);
 }
 
 // ------------------------------------------------------------ dispatch
@@ -1902,6 +2036,18 @@ static hipError_t launch_fused_grouped_t(const Args1x16<1>& a, uint32_t* ws, flo
   Args1x16<1> args = a;
   void* params[] = {&args, &ws, &amax_out};
   // a plain launch of the resident grid, as for the per-tensor fused kernel
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
+}
+
+template <int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
+static hipError_t launch_fused_list_t(const Args1x16<kMaxList>& a, uint32_t* ws, hipStream_t s) {
+  static_assert(GRAN == kGranTensor && OUT == kOutQdq, "fused list: per-tensor QDQ only");
+  auto* fn = &k_fused_list<DT, RECIPE, METRIC, PREC, ORDER>;
+  static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
+  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  Args1x16<kMaxList> args = a;
+  void* params[] = {&args, &ws};
+  // a plain launch of the resident grid, as for the other fused kernels
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 
@@ -1999,6 +2145,13 @@ hipError_t launch_qdq_1x16(int dt, int recipe, int metric, int prec, int order, 
                            const Args1x16<kMaxList>& a, hipStream_t s) {
   if (gran == kGranTensor) { FOS_DTYPES(FOS_MODES, kGranTensor, kOutQdq, CALL_QL) }
   FOS_DTYPES(FOS_MODES, kGranRow, kOutQdq, CALL_QL)
+}
+
+#define CALL_FL(DT, R, M, P, O, G, OUT) launch_fused_list_t<DT, R, M, P, O, G, OUT>(a, ws, s)
+
+hipError_t launch_fused_list(int dt, int recipe, int metric, int prec, int order, const Args1x16<kMaxList>& a,
+                             uint32_t* ws, hipStream_t s) {
+  FOS_DTYPES(FOS_MODES, kGranTensor, kOutQdq, CALL_FL)
 }
 
 #define CALL_C(DT, R, M, P, O, G, OUT) launch_colwise_t<DT, R, M, P, O, G, OUT>(a, s)

@@ -13,7 +13,7 @@ knob sweeps run on sampled rows in test_gpu_fullsize.py):
   - 16x16 weights bf16 4096x14336 and fp32 4096x4096: per-tensor MSE exact
     448;
   - the fused-QDQ expert list 8 x 2048x7168, bf16 and fp16: MSE FP16-error
-    448;
+    448, with the amaxes given and with them computed in the same launch;
   - the grouped MoE tokens 65536 (+4096 padding) x 7168, 64 groups: MSE
     exact at bounds 448 and 256, and the fused group amaxes at 448.
 """
@@ -94,8 +94,15 @@ def test_qdq_expert_list_whole(orc, dtype):
     ys = [torch.full_like(t, float("nan")) for t in xs]  # sentinel: NaN never appears in a QDQ output
     kw = dict(recipe="4over6", err_metric="mse", err_prec="fp16", bound=448)
     fos.fos_qdq_list(xs, [torch.from_numpy(a).to("cuda") for a in ams], outs=ys, **kw)
+    want = [orc.qdq(bits[i], dtype, ams[i], **kw) for i in range(8)]
     for i in range(8):
-        _eq(ys[i], orc.qdq(bits[i], dtype, ams[i], **kw), f"tensor {i} {dtype}")
+        _eq(ys[i], want[i], f"tensor {i} {dtype}")
+    # every amax and the QDQ in one launch
+    ys = [torch.full_like(t, float("nan")) for t in xs]
+    _, amax = fos.fos_qdq_list_fused(xs, outs=ys, check=True, **kw)
+    _eq(amax, np.concatenate(ams), f"fused list amaxes {dtype}")
+    for i in range(8):
+        _eq(ys[i], want[i], f"fused list tensor {i} {dtype}")
 
 
 def test_grouped_moe_whole(orc):

@@ -103,6 +103,31 @@ def test_grouped_fused_after_a_timeout(orc):
     assert int(status.item()) == 0
 
 
+def test_list_fused_after_a_timeout(orc):
+    """The fused amaxes + QDQ list shares the grouped call's banked slots: a
+    list call whose barrier gave up is followed by list calls on smaller
+    data that match the oracle (both banks)."""
+    big = [(synthdata.weight(512, 1024, 90 + i, "bf16").to(torch.float32) * 1000.0).to(torch.bfloat16)
+           for i in range(4)]
+    xs = [synthdata.weight(512, 1024, 95 + i, "bf16") for i in range(4)]
+    bits = [raw_bits(x) for x in xs]
+    want_a = [orc.amax(b, "bf16", "tensor") for b in bits]
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with poll_limit(0):
+        fos.fos_qdq_list_fused([dev(t) for t in big], workspace=ws, status=status, recipe="4over6")
+        torch.cuda.synchronize()
+    assert int(status.item()) & fos.STATUS_BARRIER_TIMEOUT, "the forced timeout did not show"
+    status.zero_()
+    for _ in range(2):
+        ys, amax = fos.fos_qdq_list_fused([dev(t) for t in xs], workspace=ws, status=status, recipe="4over6")
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert amax.cpu().numpy().view(np.uint32)[i] == want_a[i].view(np.uint32)[0]
+            np.testing.assert_array_equal(raw_bits(ys[i].cpu()), orc.qdq(bits[i], "bf16", want_a[i], recipe="4over6"))
+    assert int(status.item()) == 0
+
+
 def test_checked_mode_raises_on_timeout(orc):
     """check=True synchronizes and raises when the barrier gave up; the
     binding's own status word is cleared by the check, and a checked call

@@ -238,6 +238,79 @@ def test_qdq_single_and_many_tensors(orc):
     np.testing.assert_array_equal(bits_of(y0), bits_of(ys[0]))
 
 
+def _fused_list_inputs(dtype):
+    """A list with ragged widths, a one-block tensor, an empty tensor, an
+    all-zero tensor, one with NaN and infinities, and one spanning several
+    units per wave."""
+    shapes = [(64, 1024), (48, 272), (1, 16), (0, 32), (200, 4112), (32, 64), (96, 160), (16, 2048)]
+    xs = []
+    for i, (M, K) in enumerate(shapes):
+        t = synthdata.activation_family("outlier", max(M, 1), K, 300 + i, dtype).to(torch.float32)[:M]
+        if i == 5:
+            t.zero_()
+        if i == 6:
+            t[3, 7] = float("nan")
+            t[50, :16] = float("nan")
+            t[10, 9] = float("inf")
+            t[11, 0] = -float("inf")
+        xs.append(t.to(synthdata.TORCH_DTYPES[dtype]).contiguous())
+    return xs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_qdq_list_fused(orc, dtype):
+    """Every tensor's amax and the QDQ of the list in one launch equal the
+    oracle's amax of each tensor followed by its QDQ, bit for bit, for every
+    mode and both orders; one workspace across the calls."""
+    xs = _fused_list_inputs(dtype)
+    bits = [raw_bits(x) for x in xs]
+    want_a = [orc.amax(b, dtype, "tensor") if b.size else np.zeros(1, np.float32) for b in bits]
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xd = [dev(x) for x in xs]
+    modes = [(r, m, p, o) for (r, m, p) in MODES for o in (("tree", "seq") if r == "4over6" else ("tree",))]
+    for (recipe, metric, prec, order), bound in itertools.product(modes, (448, 256)):
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, bound=bound, err_order=order)
+        ys = [torch.full_like(x, float("nan")) for x in xd]
+        ys, amax = fos.fos_qdq_list_fused(xd, outs=ys, workspace=ws, status=status, **kw)
+        torch.cuda.synchronize()
+        got_a = amax.cpu().numpy().view(np.uint32)
+        for i, (b, a) in enumerate(zip(bits, want_a)):
+            assert got_a[i] == a.view(np.uint32)[0], f"amax of tensor {i} {kw}"
+            if b.size:
+                np.testing.assert_array_equal(u_bits(bits_of(ys[i])), u_bits(orc.qdq(b, dtype, a, **kw)),
+                                              err_msg=f"tensor {i} {kw}")
+    assert int(status.item()) == 0
+
+
+def test_qdq_list_fused_many_tensors_and_shared_workspace(orc):
+    """53 tensors (two launches), with a grouped fused call on the same
+    workspace between list calls (the two share the banked slots)."""
+    xs = [synthdata.weight(16 + 16 * (i % 3), 64 + 16 * (i % 5), 400 + i, "bf16") for i in range(53)]
+    bits = [raw_bits(x) for x in xs]
+    want_a = [orc.amax(b, "bf16", "tensor") for b in bits]
+    x, offs, _ = synthdata.grouped_tokens(512, 32, 128, 8, seeds=(71, 72, 73, 74), dtype="bf16")
+    gb = raw_bits(x)
+    starts = np.concatenate([[0], offs[:-1]])
+    gam = np.array([orc.amax(gb[s:e], "bf16", "tensor")[0] if e > s else 0.0 for s, e in zip(starts, offs)],
+                   np.float32)
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xd = [dev(t) for t in xs]
+    for rep in range(3):
+        kw = dict(recipe="4over6", err_metric=("mse", "mae", "mse")[rep], err_prec=("fp16", "exact", "exact")[rep])
+        ys, amax = fos.fos_qdq_list_fused(xd, workspace=ws, status=status, **kw)
+        _, _, ga, _ = fos.fos_quantize_grouped_fused(dev(x), dev(torch.from_numpy(offs)), workspace=ws,
+                                                     status=status, recipe="4over6")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ga.cpu().numpy().view(np.uint32), gam.view(np.uint32))
+        got_a = amax.cpu().numpy().view(np.uint32)
+        for i in range(53):
+            assert got_a[i] == want_a[i].view(np.uint32)[0], f"amax {i}"
+            np.testing.assert_array_equal(bits_of(ys[i]), orc.qdq(bits[i], "bf16", want_a[i], **kw), err_msg=f"{i}")
+    assert int(status.item()) == 0
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("gran", ["tensor", "row"])
 def test_dequantize(orc, out_dtype, gran):
