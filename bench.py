@@ -78,18 +78,14 @@ COUNTER_KERNELS = {
          "fos_quantize with a precomputed amax, bf16 8192x4096 N(0,1), four-over-six MSE exact, bound 448",
          _N2 * 2 + _N2 // 2 + _N2 // 16),
 }
-KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_adaptive_block_amd", "csrc", f)
-                  for f in ("fos_kernels.hip", "fos_device.h", "fos_kernels.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 HEADLINE_TRACE = os.path.join(PROFILES, "kernel_trace_quantize_grouped_bf16_65536x7168.txt")
 STREAM_LIB = os.path.join(ROOT, "libbench_stream.so")
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
+    from nvfp4_adaptive_block_amd.build import kernel_source_hash as h
+    return h()
 
 
 def read_profile_value(path, key):
@@ -124,20 +120,33 @@ def rotating(t, bytes_per_set):
     return [t.clone() for _ in range(n)]
 
 
-def time_loop(fn, n_sets, steps, warmup):
-    """Run fn(i) `warmup` times untimed, then `steps` times with an event pair
-    around each launch on the current stream; returns the per-launch ms."""
+def time_loop(fn, n_sets, steps, warmup, reps=3):
+    """Per-launch device time of fn: `warmup` untimed calls, then `steps`
+    calls (buffer set i % n_sets) captured into one HIP graph, replayed
+    `reps` times between two events; returns each replay's time over
+    `steps`, in ms. The graph runs the launches back to back, so host-side
+    call overhead (argument marshalling, a few to tens of microseconds per
+    call) does not enter the time of short kernels."""
     import torch
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record()
-        fn(i % n_sets)
-        evs[i][1].record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i % n_sets)
+    g.replay()
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / steps)
+    del g
+    return out
 
 
 def gbs(nbytes, ms):
@@ -376,8 +385,9 @@ def cpu_leg(args, x_host, offs, gam_dev, codes, scales, raw_bits, np):
 
 def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
     """Brief kernel-only timings of the other configurations; each figure is
-    the median launch of its loop, over the algorithmic bytes: every input
-    read once and every output written once."""
+    the median over graph replays of the mean launch time (time_loop), over
+    the algorithmic bytes: every input read once and every output written
+    once."""
     out = {}
     xd, od, gam, c, s = c5
 
@@ -396,8 +406,11 @@ def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
                                                                       err_metric="mse", bound=256), 1, steps, warmup)))
     out[f"quantize_grouped_{M5}+{PAD5}x{K5}_G{G5}_256"] = entry(STEP_BYTES, ms)
     ga = torch.empty(G5, dtype=torch.float32, device="cuda")
+    gws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    gst = torch.zeros(1, dtype=torch.int32, device="cuda")
     ms = float(np.median(time_loop(lambda i: fos.fos_quantize_grouped_fused(xd, od, codes=c, scales=s, group_amax=ga,
-                                                                            **KNOBS), 1, steps, warmup)))
+                                                                            workspace=gws, status=gst, **KNOBS),
+                                   1, steps, warmup)))
     out[f"fused_group_amax_quantize_grouped_{M5}+{PAD5}x{K5}_G{G5}_448"] = entry(
         STEP_BYTES, ms, note="one launch; its amax phase reads the data rows a second time")
     log(f"[bench] grouped: {out}")
@@ -432,8 +445,8 @@ def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
     runs["quantize_1x16_bf16_8192x4096_per_row_amax"] = (
         lambda i: fos.fos_quantize(xs[i], row_amax[i], codes=codes[i], scales=scales[i], **rk), qb, None)
     runs["fused_row_amax_quantize_bf16_8192x4096"] = (
-        lambda i: fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=ra, **rk), qb,
-        "one launch, each row read once")
+        lambda i: fos.fos_quantize_fused(xs[i], codes=codes[i], scales=scales[i], amax=ra, workspace=ws, status=st,
+                                         **rk), qb, "one launch, each row read once")
     ct = torch.empty(K, M // 2, dtype=torch.uint8, device="cuda")
     stt = torch.empty(K, M // 16, dtype=torch.uint8, device="cuda")
     runs["quantize_columnwise_bf16_8192x4096"] = (
@@ -504,7 +517,7 @@ def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
                                              note="one launch: every amax, then the QDQ; x read twice")
             log(f"[bench] fused_amax_{key}: {ms * 1e3:.2f} us, {gbs(nbytes, ms)} GB/s")
         del sets, ys, ams, base
-    out["fused_calls_status_clean"] = int(lst_status.item()) == 0 and int(st.item()) == 0
+    out["fused_calls_status_clean"] = int(lst_status.item()) == 0 and int(st.item()) == 0 and int(gst.item()) == 0
     return out
 
 
@@ -672,13 +685,23 @@ def alg_blocks(stem: str) -> int:
             "quantize_1x16_bf16_8192x4096": _N2 // 16}[stem]
 
 
-def static_occupancy(vgpr: int, lds: int, wg: int) -> int:
-    """Waves per SIMD the registers and LDS allow (512 VGPRs per lane and
-    SIMD in granules of 8, at most 8 waves; 160 KiB of LDS per CU)."""
-    by_vgpr = min(8, 512 // max(8, -(-vgpr // 8) * 8))
-    waves_per_wg = max(1, wg // 64)
-    by_lds = 8 if lds == 0 else (160 * 1024 // lds) * waves_per_wg // 4
-    return max(0, min(by_vgpr, by_lds))
+RESOURCES = os.path.join(PROFILES, "kernel_resources_gfx950.txt")
+
+
+def kernel_resources(kernel: str, path: str | None = None) -> dict:
+    """The compiler's resource figures of one kernel instance (VGPRs, SGPRs,
+    spills, LDS, the waves per SIMD they allow) from the committed summary,
+    or {} when it is absent or was taken on other kernel code."""
+    path = path or RESOURCES
+    if not os.path.exists(path):
+        return {}
+    lines = open(path).read().splitlines()
+    if f"# kernel_source_sha256_16 = {kernel_source_hash()}" not in lines:
+        return {}
+    for line in lines:
+        if line.startswith(kernel + " |"):
+            return dict(kv.split("=", 1) for kv in line.split("|", 1)[1].split())
+    return {}
 
 
 def provenance(agent_csv=None):
@@ -734,8 +757,8 @@ def write_profiles(d, out_dir=PROFILES):
               f"headline_kernel_calls = {len(durs)}",
               f"headline_kernel_avg_us = {sum(durs) / len(durs) / 1e3:.2f}",
               f"headline_kernel_median_us = {sorted(durs)[len(durs) // 2] / 1e3:.2f}",
-              f"vgpr_count = {v}", f"lds_bytes_per_workgroup = {l}", f"grid_threads = {g}", f"workgroup = {wg}",
-              f"static_occupancy_waves_per_simd = {static_occupancy(v, l, wg)}",
+              f"grid_threads = {g}", f"workgroup = {wg}",
+              *(f"compiler_{k} = {val}" for k, val in kernel_resources(HEADLINE_KERNEL).items()),
               f"algorithmic_bytes_per_launch = {STEP_BYTES}",
               f"achieved_GBs_at_avg = {STEP_BYTES / (sum(durs) / len(durs)) :.1f}"]
     open(os.path.join(out_dir, os.path.basename(HEADLINE_TRACE)), "w").write("\n".join(lines) + "\n")
@@ -785,8 +808,8 @@ def write_profiles(d, out_dir=PROFILES):
                  f"hbm_read_bytes_per_launch = {rd:.0f}", f"hbm_write_bytes_per_launch = {wr:.0f}",
                  f"hbm_bytes_per_launch = {rd + wr:.0f}", f"algorithmic_bytes_per_launch = {alg}",
                  f"traffic_over_algorithmic = {(rd + wr) / alg:.4f}",
-                 f"vgpr_count = {v}", f"lds_bytes_per_workgroup = {l}", f"grid_threads = {g}",
-                 f"static_occupancy_waves_per_simd = {static_occupancy(v, l, wg)}",
+                 f"grid_threads = {g}",
+                 *(f"compiler_{k} = {val}" for k, val in kernel_resources(kernel).items()),
                  f"occupancy_percent = {occ_pct:.1f}   # rocprofv3 OccupancyPercent (of 32 waves per CU)",
                  f"occupancy_waves_per_simd = {occ_pct / 100 * 8:.2f}",
                  f"valu_busy = {mean(occ[(kernel, 'VALUBusy')]) / 100:.4f}   # rocprofv3 VALUBusy",

@@ -67,10 +67,13 @@ def test_step_bytes_of_the_grouped_step():
             assert alg == blocks * 41
 
 
-def test_static_occupancy():
-    occ = bench.static_occupancy
-    assert occ(64, 0, 256) == 8
-    assert occ(87, 0, 256) == 5      # 88 VGPRs: 512 // 88
-    assert occ(128, 0, 256) == 4
-    assert occ(87, 36864, 256) == 4  # 4 workgroups of 36 KiB per CU: 16 waves
-    assert occ(200, 0, 256) == 2
+def test_kernel_resources_need_the_current_kernel_sources(tmp_path):
+    name = bench.HEADLINE_KERNEL
+    good = tmp_path / "good.txt"
+    good.write_text(f"# kernel_source_sha256_16 = {bench.kernel_source_hash()}\n"
+                    f"{name} | sgprs=106 vgprs=95 occupancy_waves_per_simd=5\n")
+    stale = tmp_path / "stale.txt"
+    stale.write_text(f"# kernel_source_sha256_16 = 0000000000000000\n{name} | vgprs=95\n")
+    assert bench.kernel_resources(name, str(good)) == {"sgprs": "106", "vgprs": "95", "occupancy_waves_per_simd": "5"}
+    assert bench.kernel_resources("void fos::k_other<0>(int)", str(good)) == {}
+    assert bench.kernel_resources(name, str(stale)) == {}
