@@ -642,13 +642,20 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
   }
 }
 
-// The wave's share [u, u_end) of units [begin, end): contiguous ranges of
-// equal size, in wave order.
+// The wave's share [u, u_end) of units [begin, end): contiguous ranges in
+// wave order, of n / nwaves units and one more for the first n % nwaves
+// waves. Waves are numbered round by round (workgroup b holds waves 4b ..
+// 4b + 3, and the dispatcher deals workgroups out over the CUs in turn), so
+// the longer ranges spread evenly over the SIMDs: each SIMD's total differs
+// by at most a unit per round. (Ranges of ceil(n / nwaves) units would leave
+// the last waves idle and load the SIMDs that hold none of them with up to
+// a unit per wave more.)
 __device__ __forceinline__ void wave_range(int64_t begin, int64_t end, int64_t wave, int64_t nwaves, int64_t& u,
                                            int64_t& u_end) {
-  const int64_t per = (end - begin + nwaves - 1) / nwaves;
-  u = min(end, begin + wave * per);
-  u_end = min(end, u + per);
+  const int64_t n = max(end - begin, (int64_t)0);
+  const int64_t base = n / nwaves, extra = n - base * nwaves;
+  u = begin + wave * base + min(wave, extra);
+  u_end = u + base + (wave < extra ? 1 : 0);
 }
 
 // Units of a grouped launch that hold data rows (rows before offs[G-1]);
@@ -762,13 +769,14 @@ __device__ __forceinline__ float lane_tree(float* w) {
   return w[0];
 }
 
-// Quantize the lane's rows of one tile. raw[i] holds row j + LPT i.
-// Returns false when the fast form cannot be trusted (a NaN in the tile);
-// the caller then reruns with CAREFUL. The kept candidate is the same on all
-// lanes of the group.
-template <int DT, int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT>
-__device__ __forceinline__ bool tile_rows(const Raw<DT>* raw, float S_enc, float S_dec, const Table& tab,
-                                          uint32_t (*codes)[2], uint32_t& scale, float (*xh)[16]) {
+// Quantize the lane's rows of one tile. raw[i] holds row j + LPT i; done(i)
+// runs as soon as raw[i] is no longer needed (the caller refills it with the
+// next unit's row). Returns false when the fast form cannot be trusted (a
+// NaN in the tile); the caller then reruns with CAREFUL on the same rows. The
+// kept candidate is the same on all lanes of the group.
+template <int DT, int RECIPE, int METRIC, int PREC, bool CAREFUL, bool NEED_XHAT, class Done>
+__device__ __forceinline__ bool tile_rows(Raw<DT>* raw, float S_enc, float S_dec, const Table& tab,
+                                          uint32_t (*codes)[2], uint32_t& scale, float (*xh)[16], Done done) {
   constexpr int kLPT = Tile16<DT>::kLPT, kRPL = Tile16<DT>::kRPL;
   // NaN-dropping tile amax; 16-bit inputs straight from their bits (no
   // unpacked row stays live for the encode loop)
@@ -802,6 +810,7 @@ __device__ __forceinline__ bool tile_rows(const Raw<DT>* raw, float S_enc, float
       encode16<CAREFUL>(x, k6.E, codes[i][0], codes[i][1]);
       if (NEED_XHAT) decode16(codes[i][0], codes[i][1], k6.D, xh[i]);
       if (!CAREFUL && any_nan16(x)) nan = 1.0f;
+      done(i);
     }
     scale = k6.scale;
     return CAREFUL || group_max<kLPT>(nan) == 0.0f;
@@ -819,6 +828,7 @@ __device__ __forceinline__ bool tile_rows(const Raw<DT>* raw, float S_enc, float
       encode16<CAREFUL>(x, k4.E, c4[i][0], c4[i][1]);
       decode16(c4[i][0], c4[i][1], k4.D, t);
       r4[i] = err16<METRIC, PREC, kOrderTree>(x, t);
+      done(i);
       __builtin_amdgcn_sched_barrier(0);  // one row at a time (register pressure)
     }
     const float e6 = group_tree<kLPT>(lane_tree<kRPL>(r6));
@@ -851,9 +861,8 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   const int64_t K = args.K, nbk = K >> 4;
   const int64_t gpb = (nbk + kT - 1) / kT;  // units per band
   const int64_t total = (args.M >> 4) * gpb;
-  const int64_t per = (total + nwaves - 1) / nwaves;
-  int64_t u = wave * per;
-  const int64_t u_end = min(total, u + per);
+  int64_t u, u_end;
+  wave_range(0, total, wave, nwaves, u, u_end);
   const float six_b = args.six_b;
 
   if (OUT == kOutQuant && args.sdec_out) {
@@ -916,13 +925,16 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
     for (int i = 0; i < kRPL; i++) raw[i].load(U.x, U.active ? ox0 + i * ox_step : kOOB);
   };
 
-  // one unit at a time: prefetching the next unit's rows costs more
-  // occupancy than the overlap gains (measured)
+  // The next unit's rows load while this unit is quantized, each into the
+  // registers of a row as soon as the row is done (no registers beyond the
+  // one unit's rows). A tile that needs the careful form reloads its rows.
   P16 p{u / gpb, u % gpb};
+  U16 U = unit(p, true);
+  Raw<DT> raw[kRPL];
+  load(raw, U);
   for (; u < u_end; u++) {
-    const U16 U = unit(p, true);
-    Raw<DT> raw[kRPL];
-    load(raw, U);
+    const P16 pn = advance(p);
+    const U16 Un = unit(pn, u + 1 < u_end);
     if (GRAN == kGranRow && p.band != cur_band) {
       // tile-uniform contract: the band uses its first row's amax, and a band
       // whose rows differ is flagged
@@ -941,8 +953,12 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
     }
     uint32_t codes[kRPL][2], scale;
     float xh[kXhat ? kRPL : 1][16];
-    if (!tile_rows<DT, RECIPE, METRIC, PREC, false, kXhat>(raw, S_enc, S_dec, tab, codes, scale, xh))
-      tile_rows<DT, RECIPE, METRIC, PREC, true, kXhat>(raw, S_enc, S_dec, tab, codes, scale, xh);
+    auto refill = [&](int i) { raw[i].load(Un.x, Un.active ? ox0 + i * ox_step : kOOB); };
+    if (!tile_rows<DT, RECIPE, METRIC, PREC, false, kXhat>(raw, S_enc, S_dec, tab, codes, scale, xh, refill)) {
+      load(raw, U);
+      tile_rows<DT, RECIPE, METRIC, PREC, true, kXhat>(raw, S_enc, S_dec, tab, codes, scale, xh, [](int) {});
+      load(raw, Un);
+    }
 #pragma unroll
     for (int i = 0; i < kRPL; i++) {
       if (OUT == kOutQuant) {
@@ -952,7 +968,8 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
         store16<DT>(U.out, U.active ? ox0 + i * ox_step : kOOB, xh[i]);
       }
     }
-    p = advance(p);
+    p = pn;
+    U = Un;
   }
 }
 
@@ -1454,9 +1471,8 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
   const Table tab{lds[wv], lds[wv] + 128};
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
-  const int64_t u = min(args.total_units, wave * per);
-  const int64_t u_end = min(args.total_units, u + per);
+  int64_t u, u_end;  // at most ceil(total_units / nwaves) units
+  wave_range(0, args.total_units, wave, nwaves, u, u_end);
   const TensorRef& T = args.t[0];
   const int64_t nblk = T.M * (T.K >> 4);
 
@@ -1572,9 +1588,8 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   const Table tab{lds[wv], lds[wv] + 128};
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (args.total_units + nwaves - 1) / nwaves;  // <= onchip_units (the launch checks)
-  const int64_t u = min(args.total_units, wave * per);
-  const int64_t u_end = min(args.total_units, u + per);
+  int64_t u, u_end;  // at most ceil(total_units / nwaves) units
+  wave_range(0, args.total_units, wave, nwaves, u, u_end);
   const TensorRef& T = args.t[0];
   const int64_t nblk = T.M * (T.K >> 4);
   const Walk<DT, kGranTensor, OUT> W(T, args.codes, args.scales);
@@ -1898,9 +1913,8 @@ __global__ void __launch_bounds__(256) k_fused_list(const Args1x16<kMaxList> arg
   const int n = args.n;
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = (args.total_units + nwaves - 1) / nwaves;
-  const int64_t u = min(args.total_units, wave * per);
-  const int64_t u_end = min(args.total_units, u + per);
+  int64_t u, u_end;  // at most ceil(total_units / nwaves) units
+  wave_range(0, args.total_units, wave, nwaves, u, u_end);
 
   for (int t = threadIdx.x; t < n; t += blockDim.x) gm[t] = 0u;
   if (threadIdx.x == 0) {
@@ -1962,6 +1976,13 @@ static unsigned small_grid(int64_t n) {
 
 // Workgroups of 256 threads resident at once for kernel fn: the grid of the
 // unit-walking kernels (each wave then walks a contiguous unit range).
+static int64_t num_cus() {
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  return cus;
+}
+
 static int64_t resident_grid(const void* fn) {
   int dev = 0, cus = 0, per_cu = 0;
   (void)hipGetDevice(&dev);
@@ -1974,7 +1995,8 @@ template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN,
 static hipError_t launch_1x16_t(const Args1x16<NT>& a, hipStream_t s) {
   auto* fn = &k_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT>;
   static const int64_t resident = resident_grid(reinterpret_cast<const void*>(fn));
-  const int64_t grid = max((int64_t)1, min(resident, (a.total_units + 3) / 4));
+  static const int64_t cap = OUT == kOutQuant ? min(resident, 4 * num_cus()) : resident;
+  const int64_t grid = max((int64_t)1, min(cap, (a.total_units + 3) / 4));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
