@@ -185,13 +185,15 @@ class Stream:
         if not os.path.exists(STREAM_LIB):
             raise FileNotFoundError(f"{STREAM_LIB} is not built (run __graft_entry__.build())")
         self.lib = ctypes.CDLL(STREAM_LIB)
-        self.lib.stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        self.lib.stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         self.lib.stream_bytes_per_unit.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                                    ctypes.POINTER(ctypes.c_int64)]
 
     def measure(self, torch, np, mix, units, steps=60, warmup=10):
-        """Best median GB/s over the two store policies, and each."""
+        """Best median GB/s over the two store policies and the two unit
+        orders (contiguous ranges per wave, or pairs dealt round robin), and
+        each."""
         r, w = ctypes.c_int64(), ctypes.c_int64()
         self.lib.stream_bytes_per_unit(self.MIXES[mix], ctypes.byref(r), ctypes.byref(w))
         src = torch.empty(max(1, units * r.value), dtype=torch.uint8, device="cuda")
@@ -200,17 +202,18 @@ class Stream:
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         nbytes = units * (r.value + w.value)
         out = {}
-        for nt in (0, 1):
-            def run(_i, nt=nt):
-                rc = self.lib.stream_run(self.MIXES[mix], nt, ctypes.c_void_p(src.data_ptr()),
-                                         ctypes.c_void_p(dst.data_ptr()), units, ctypes.c_void_p(sink.data_ptr()),
-                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-                assert rc == 0
-            ms = float(np.median(time_loop(run, 1, steps, warmup)))
-            out["nt" if nt else "default"] = entry(nbytes, ms)
+        for il in (0, 1):
+            for nt in (0, 1):
+                def run(_i, nt=nt, il=il):
+                    rc = self.lib.stream_run(self.MIXES[mix], nt, il, ctypes.c_void_p(src.data_ptr()),
+                                             ctypes.c_void_p(dst.data_ptr()), units, ctypes.c_void_p(sink.data_ptr()),
+                                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                    assert rc == 0
+                ms = float(np.median(time_loop(run, 1, steps, warmup)))
+                out[("nt" if nt else "default") + ("_interleaved" if il else "")] = entry(nbytes, ms)
         best = max(out.values(), key=lambda e: e["GB/s"])
         return {"GB/s": best["GB/s"], "frac": best["frac"], "read_bytes": units * r.value,
-                "write_bytes": units * w.value, "stores": out}
+                "write_bytes": units * w.value, "variants": out}
 
 
 # ---------------------------------------------------------------- main

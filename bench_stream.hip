@@ -3,10 +3,14 @@
 // libbench_stream.so by __graft_entry__.build(); only bench.py loads it.
 //
 // They move bytes the way the 1x16 quantizer does, with nothing computed:
-// each wave walks a contiguous range of units with 128-bit raw buffer loads
-// (lane l reads 16-byte pieces l, l + 64, ... of the unit), two units in
-// flight, and writes its share of the output with 128-bit stores. Per unit
-// and lane: R loads, W stores, and one more store on the first T lanes.
+// each wave walks its units with 128-bit raw buffer loads (lane l reads
+// 16-byte pieces l, l + 64, ... of the unit), two units in flight, and
+// writes its share of the output with 128-bit stores. Per unit and lane: R
+// loads, W stores, and one more store on the first T lanes. A wave's units
+// are either one contiguous range (the quantizer's order) or pairs of
+// consecutive units dealt out round robin (wave w takes pairs w, w + nwaves,
+// ...), which keeps every wave inside one moving window of the buffers; the
+// benchmark takes the faster as the ceiling.
 // The mixes:
 //   read only              R = 4, W = 0
 //   write only             R = 0, W = 4
@@ -32,15 +36,20 @@ __device__ __forceinline__ Rsrc rsrc(const void* base, int64_t bytes) {
 }
 
 template <int R, int W, int T, int POLICY>
-__global__ void __launch_bounds__(256) k_stream(const char* src, char* dst, int64_t units, uint32_t* sink) {
+__global__ void __launch_bounds__(256) k_stream(const char* src, char* dst, int64_t units, uint32_t* sink,
+                                                int interleave) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t per = (units + nwaves - 1) / nwaves;
-  const int64_t u0 = wave * per, u1 = min(units, u0 + per);
+  // contiguous: [wave * per, + per) in steps of 2; interleaved: pairs from
+  // 2 * wave in steps of 2 * nwaves. A pair is units u and u + 1 < u1.
+  const int64_t u0 = interleave ? 2 * wave : wave * per;
+  const int64_t u1 = interleave ? units : min(units, u0 + per);
+  const int64_t step = interleave ? 2 * nwaves : 2;
   constexpr int64_t kRB = R * 1024, kWB = W * 1024 + T * 16;  // bytes per unit
   v4i acc = {0, 0, 0, 0};
-  for (int64_t u = u0; u < u1; u += 2) {
+  for (int64_t u = u0; u < u1; u += step) {
     v4i a[R > 0 ? R : 1], b[R > 0 ? R : 1];
     const Rsrc ra = rsrc(src + u * kRB, kRB), rb = rsrc(src + (u + 1) * kRB, u + 1 < u1 ? kRB : 0);
 #pragma unroll
@@ -66,7 +75,7 @@ __global__ void __launch_bounds__(256) k_stream(const char* src, char* dst, int6
 }
 
 template <int R, int W, int T, int POLICY>
-int launch(const void* src, void* dst, int64_t units, uint32_t* sink, hipStream_t s) {
+int launch(const void* src, void* dst, int64_t units, uint32_t* sink, int interleave, hipStream_t s) {
   auto* fn = &k_stream<R, W, T, POLICY>;
   int dev = 0, cus = 256, per_cu = 0;
   (void)hipGetDevice(&dev);
@@ -74,7 +83,7 @@ int launch(const void* src, void* dst, int64_t units, uint32_t* sink, hipStream_
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu <= 0) per_cu = 2;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * per_cu, (units + 3) / 4));
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const char*>(src), static_cast<char*>(dst),
-                     units, sink);
+                     units, sink, interleave);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
@@ -82,9 +91,10 @@ int launch(const void* src, void* dst, int64_t units, uint32_t* sink, hipStream_
 
 extern "C" {
 
-// mix: 0 read only, 1 write only, 2 quantize, 3 QDQ; nt: non-temporal stores.
-// Bytes per unit: read 4096 / 0 / 4096 / 2048, written 0 / 4096 / 1152 / 2048.
-// src and dst must hold units times those bytes.
+// mix: 0 read only, 1 write only, 2 quantize, 3 QDQ; nt: non-temporal stores;
+// interleave: units dealt in pairs round robin rather than as contiguous
+// ranges. Bytes per unit: read 4096 / 0 / 4096 / 2048, written 0 / 4096 /
+// 1152 / 2048. src and dst must hold units times those bytes.
 int stream_bytes_per_unit(int mix, int64_t* read, int64_t* write) {
   static const int64_t r[4] = {4096, 0, 4096, 2048}, w[4] = {0, 4096, 1152, 2048};
   if (mix < 0 || mix > 3) return 1;
@@ -93,16 +103,17 @@ int stream_bytes_per_unit(int mix, int64_t* read, int64_t* write) {
   return 0;
 }
 
-int stream_run(int mix, int nt, const void* src, void* dst, int64_t units, uint32_t* sink, void* stream) {
+int stream_run(int mix, int nt, int interleave, const void* src, void* dst, int64_t units, uint32_t* sink,
+               void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (mix * 2 + (nt ? 1 : 0)) {
-    case 0: case 1: return launch<4, 0, 0, 0>(src, dst, units, sink, s);
-    case 2: return launch<0, 4, 0, 0>(src, dst, units, sink, s);
-    case 3: return launch<0, 4, 0, 2>(src, dst, units, sink, s);
-    case 4: return launch<4, 1, 8, 0>(src, dst, units, sink, s);
-    case 5: return launch<4, 1, 8, 2>(src, dst, units, sink, s);
-    case 6: return launch<2, 2, 0, 0>(src, dst, units, sink, s);
-    case 7: return launch<2, 2, 0, 2>(src, dst, units, sink, s);
+    case 0: case 1: return launch<4, 0, 0, 0>(src, dst, units, sink, interleave, s);
+    case 2: return launch<0, 4, 0, 0>(src, dst, units, sink, interleave, s);
+    case 3: return launch<0, 4, 0, 2>(src, dst, units, sink, interleave, s);
+    case 4: return launch<4, 1, 8, 0>(src, dst, units, sink, interleave, s);
+    case 5: return launch<4, 1, 8, 2>(src, dst, units, sink, interleave, s);
+    case 6: return launch<2, 2, 0, 0>(src, dst, units, sink, interleave, s);
+    case 7: return launch<2, 2, 0, 2>(src, dst, units, sink, interleave, s);
     default: return 1;
   }
 }
