@@ -204,6 +204,44 @@ def test_16x16_special_data_and_nonuniform_flag(orc):
         assert int(status.item()) & fos.STATUS_TILE_NONUNIFORM
 
 
+@pytest.mark.parametrize("dtype,M,K,out", [("bf16", 4096, 16384, "quantize"), ("fp32", 2048, 16384, "quantize"),
+                                            ("bf16", 4096, 8192, "qdq")])
+def test_16x16_careful_tiles_between_prefetched_units(orc, dtype, M, K, out):
+    """Tiles that need the careful form (a NaN or an inf) scattered over a
+    tensor large enough that every wave takes several units: a tile whose
+    fast form fails reloads its rows after the next unit's rows were already
+    requested in their place, then requests them again. Every output must
+    still match the oracle (whole tensors compared)."""
+    w = synthdata.weight(M, K, 33, dtype).to(torch.float32)
+    a = orc.amax(raw_bits(w.to(synthdata.TORCH_DTYPES[dtype])), dtype, "tensor")  # of the finite data
+    g = torch.Generator().manual_seed(34)
+    ntiles = (M // 16) * (K // 16)
+    tiles = torch.randperm(ntiles, generator=g)[: ntiles // 200]
+    r0 = (tiles // (K // 16)) * 16 + torch.randint(0, 16, tiles.shape, generator=g)
+    c0 = (tiles % (K // 16)) * 16 + torch.randint(0, 16, tiles.shape, generator=g)
+    half = tiles.numel() // 2
+    w[r0[:half], c0[:half]] = float("nan")
+    w[r0[half:], c0[half:]] = float("inf")
+    w[0:16, 0:16] = float("nan")  # one all-NaN tile
+    x = w.to(synthdata.TORCH_DTYPES[dtype])
+    b = raw_bits(x)
+    xd, ad = dev(x), dev(torch.from_numpy(a))
+    modes = [("4over6", "mse", "exact"), ("4over6", "mae", "fp16"), ("nvfp4", "mse", "exact")]
+    for recipe, metric, prec in modes:
+        kw = dict(recipe=recipe, err_metric=metric, err_prec=prec, block="16x16")
+        if out == "quantize":
+            want = orc.quantize(b, dtype, a, **kw)
+            codes, scales, _ = fos.fos_quantize(xd, ad, **kw)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"], err_msg=f"scales {kw}")
+            np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"], err_msg=f"codes {kw}")
+        else:
+            want = orc.qdq(b, dtype, a, **kw)
+            y = fos.fos_qdq(xd, ad, **kw)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(bits_of(y), want, err_msg=f"qdq {kw}")
+
+
 # ------------------------------------------------------------------ QDQ and dequantize
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
