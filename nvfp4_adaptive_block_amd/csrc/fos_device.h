@@ -15,8 +15,9 @@
 //   - E2M1 pair -> f32 (v_cvt_scalef32_pk_f32_fp4, scale 1.0): exact.
 //   - f32 -> E4M3 (v_cvt_pk_fp8_f32) on inputs clamped to [0, 448]: RNE.
 //   - E4M3 -> f32 (v_cvt_f32_fp8): exact.
-//   - f32 -> f16 and f32 -> bf16 (v_cvt_f16_f32, v_cvt_pk_bf16_f32): RNE,
-//     overflow to inf, gradual underflow.
+//   - f32 pair -> f16 pair and f32 pair -> bf16 pair (v_cvt_pk_f16_f32,
+//     v_cvt_pk_bf16_f32): RNE, overflow to inf, gradual underflow, in
+//     either half.
 // The build uses -ffp-contract=off and HIP's correctly rounded f32 division.
 #pragma once
 
@@ -52,14 +53,19 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)h;
 }
 
-// two binary32 -> packed bf16 pair / f16 pair (RNE)
+// two binary32 -> packed bf16 pair / f16 pair (RNE), one packed convert
+// each (written out: from two scalar casts the compiler emits two converts,
+// a shift and an OR). Both halves round as the scalar casts do, checked on
+// every binary32 input in either position.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  __bf16 a = (__bf16)opaque(lo), b = (__bf16)opaque(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-  _Float16 a = (_Float16)opaque(lo), b = (_Float16)opaque(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 
 // ---------------------------------------------------------------- scales
@@ -129,16 +135,16 @@ __device__ __forceinline__ float div6(float a) {
   return q;
 }
 
-// RN(x - f32(RN16(xh))): the error of x against the decoded value rounded to
-// binary16 (FP16-error mode).
-__device__ __forceinline__ float sub_f16(float x, float xh) {
-  // x - f32(h) as one mixed-precision FMA: the product h * -1 is exact and the
-  // FMA rounds once, so this is RN(x - f32(h)) with the same signed zeros
-  // (the compiler turns fma(h, -1, x) back into a convert and a subtract)
-  const _Float16 h = (_Float16)opaque(xh);
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
+// RN(x - f32(RN16(xh))) for two elements: the error of x against the
+// decoded value rounded to binary16 (FP16-error mode). One packed convert
+// rounds both decoded values to binary16; each difference is then one
+// mixed-precision FMA, h * -1 + x, whose product is exact and which rounds
+// once, so it is RN(x - f32(h)) with the same signed zeros (op_sel picks the
+// high half for the second element).
+__device__ __forceinline__ void sub_f16x2(float x0, float x1, float xh0, float xh1, float& e0, float& e1) {
+  const uint32_t h = pack_f16(xh0, xh1);
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(e0) : "v"(h), "v"(x0));
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(e1) : "v"(h), "v"(x1));
 }
 
 // ---------------------------------------------------------------- reductions

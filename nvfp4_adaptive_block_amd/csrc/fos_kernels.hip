@@ -330,9 +330,16 @@ template <int METRIC, int PREC, int ORDER>
 __device__ __forceinline__ float err16(const float* x, const float* xh) {
   float u[16];
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const float e = (PREC == kErrFP16) ? sub_f16(x[i], xh[i]) : x[i] - xh[i];
-    u[i] = (METRIC == kMAE) ? __builtin_fabsf(e) : e * e;
+  for (int i = 0; i < 16; i += 2) {
+    float e0, e1;
+    if (PREC == kErrFP16) {
+      sub_f16x2(x[i], x[i + 1], xh[i], xh[i + 1], e0, e1);
+    } else {
+      e0 = x[i] - xh[i];
+      e1 = x[i + 1] - xh[i + 1];
+    }
+    u[i] = (METRIC == kMAE) ? __builtin_fabsf(e0) : e0 * e0;
+    u[i + 1] = (METRIC == kMAE) ? __builtin_fabsf(e1) : e1 * e1;
   }
   return ORDER == kOrderSeq ? seq16(u) : tree16(u);
 }

@@ -83,12 +83,17 @@ __global__ void k_div_mul(const float* a, const float* b, int64_t n, float* q, f
   p[i] = fos::opaque(a[i]) * fos::opaque(b[i]);
 }
 
-// bf16 / f16 packing of the binary32 patterns base + 2 t, base + 2 t + 1
-__global__ void k_pack16(int f16, uint32_t base, int64_t npairs, uint32_t* out) {
+// bf16 / f16 packing of the binary32 patterns base + 2 t, base + 2 t + 1;
+// the pair is also packed swapped, and any difference between a value's
+// rounding in the low and in the high half sets *mismatch
+__global__ void k_pack16(int f16, uint32_t base, int64_t npairs, uint32_t* out, uint32_t* mismatch) {
   const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (t >= npairs) return;
   const float lo = __uint_as_float(base + (uint32_t)(2 * t)), hi = __uint_as_float(base + (uint32_t)(2 * t + 1));
-  out[t] = f16 ? fos::pack_f16(lo, hi) : fos::pack_bf16(lo, hi);
+  const uint32_t r = f16 ? fos::pack_f16(lo, hi) : fos::pack_bf16(lo, hi);
+  const uint32_t q = f16 ? fos::pack_f16(hi, lo) : fos::pack_bf16(hi, lo);
+  out[t] = r;
+  if (((q >> 16) | (q << 16)) != r) atomicOr(mismatch, 1u);
 }
 
 // exact upcasts of every 16-bit pattern pair (w = 2 t | (2 t + 1) << 16)
@@ -100,23 +105,42 @@ __global__ void k_upcast16(int f16, float* out) {
   out[2 * t + 1] = f16 ? fos::f16_hi(w) : fos::bf16_hi(w);
 }
 
-// FP16-error difference x - f32(RN16(xh)) over pairs p = base + i: x is the
-// 16-bit pattern p >> 16 of the input type (bf16 or f16), xh the f16 value of
-// the pattern p & 0xFFFF
-__global__ void k_sub_f16_pairs(int x_f16, uint32_t base, int64_t n, float* out) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= n) return;
-  const uint32_t p = base + (uint32_t)i;
-  const uint32_t xw = p >> 16;
-  const float x = x_f16 ? fos::f16_lo(xw) : fos::bf16_lo(xw);
-  const float xh = fos::f16_lo(p & 0xFFFFu);
-  out[i] = fos::sub_f16(x, xh);
+// Two items of the FP16-error difference through sub_f16x2, first in the
+// order (a, b), then swapped: out gets the first results, and a value that
+// differs between the low and the high half sets *mismatch (NaN agrees with
+// any NaN).
+__device__ void sub_pair(float xa, float xb, float ha, float hb, float* out, int64_t i, uint32_t* mismatch) {
+  float ea, eb, fb, fa;
+  fos::sub_f16x2(xa, xb, ha, hb, ea, eb);
+  fos::sub_f16x2(xb, xa, hb, ha, fb, fa);
+  out[i] = ea;
+  out[i + 1] = eb;
+  const bool same_a = __float_as_uint(ea) == __float_as_uint(fa) || (ea != ea && fa != fa);
+  const bool same_b = __float_as_uint(eb) == __float_as_uint(fb) || (eb != eb && fb != fb);
+  if (!(same_a && same_b)) atomicOr(mismatch, 1u);
+}
+
+// FP16-error difference x - f32(RN16(xh)) over items p = base + i (n even):
+// x is the 16-bit pattern p >> 16 of the input type (bf16 or f16), xh the
+// f16 value of the pattern p & 0xFFFF; thread t takes items 2t and 2t + 1
+__global__ void k_sub_f16_pairs(int x_f16, uint32_t base, int64_t n, float* out, uint32_t* mismatch) {
+  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (2 * t >= n) return;
+  float x[2], xh[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const uint32_t p = base + (uint32_t)(2 * t + k);
+    const uint32_t xw = p >> 16;
+    x[k] = x_f16 ? fos::f16_lo(xw) : fos::bf16_lo(xw);
+    xh[k] = fos::f16_lo(p & 0xFFFFu);
+  }
+  sub_pair(x[0], x[1], xh[0], xh[1], out, 2 * t, mismatch);
 }
 
 // The same on given binary32 operands (fp32 inputs, xh not a binary16 value)
-__global__ void k_sub_f16(const float* x, const float* xh, int64_t n, float* out) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i < n) out[i] = fos::sub_f16(x[i], xh[i]);
+__global__ void k_sub_f16(const float* x, const float* xh, int64_t n, float* out, uint32_t* mismatch) {
+  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (2 * t < n) sub_pair(x[2 * t], x[2 * t + 1], xh[2 * t], xh[2 * t + 1], out, 2 * t, mismatch);
 }
 
 int done(void) { return hipGetLastError() == hipSuccess ? 0 : 1; }
@@ -153,20 +177,25 @@ int prim_div_mul(const float* a, const float* b, int64_t n, float* q, float* p, 
   hipLaunchKernelGGL(k_div_mul, dim3(grid_for(n)), dim3(kBlock), 0, (hipStream_t)s, a, b, n, q, p);
   return done();
 }
-int prim_pack16(int f16, uint32_t base, int64_t npairs, uint32_t* out, void* s) {
-  hipLaunchKernelGGL(k_pack16, dim3(grid_for(npairs)), dim3(kBlock), 0, (hipStream_t)s, f16, base, npairs, out);
+int prim_pack16(int f16, uint32_t base, int64_t npairs, uint32_t* out, uint32_t* mismatch, void* s) {
+  hipLaunchKernelGGL(k_pack16, dim3(grid_for(npairs)), dim3(kBlock), 0, (hipStream_t)s, f16, base, npairs, out,
+                     mismatch);
   return done();
 }
 int prim_upcast16(int f16, float* out65536, void* s) {
   hipLaunchKernelGGL(k_upcast16, dim3(grid_for(32768)), dim3(kBlock), 0, (hipStream_t)s, f16, out65536);
   return done();
 }
-int prim_sub_f16_pairs(int x_f16, uint32_t base, int64_t n, float* out, void* s) {
-  hipLaunchKernelGGL(k_sub_f16_pairs, dim3(grid_for(n)), dim3(kBlock), 0, (hipStream_t)s, x_f16, base, n, out);
+// n must be even (items are taken in pairs)
+int prim_sub_f16_pairs(int x_f16, uint32_t base, int64_t n, float* out, uint32_t* mismatch, void* s) {
+  if (n & 1) return 1;
+  hipLaunchKernelGGL(k_sub_f16_pairs, dim3(grid_for(n / 2)), dim3(kBlock), 0, (hipStream_t)s, x_f16, base, n, out,
+                     mismatch);
   return done();
 }
-int prim_sub_f16(const float* x, const float* xh, int64_t n, float* out, void* s) {
-  hipLaunchKernelGGL(k_sub_f16, dim3(grid_for(n)), dim3(kBlock), 0, (hipStream_t)s, x, xh, n, out);
+int prim_sub_f16(const float* x, const float* xh, int64_t n, float* out, uint32_t* mismatch, void* s) {
+  if (n & 1) return 1;
+  hipLaunchKernelGGL(k_sub_f16, dim3(grid_for(n / 2)), dim3(kBlock), 0, (hipStream_t)s, x, xh, n, out, mismatch);
   return done();
 }
 

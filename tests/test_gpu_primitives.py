@@ -50,10 +50,10 @@ _SIGS = {
     "prim_div6": [_U32, _I64, _P, _P],
     "prim_global_scales": [_U32, _I64, ctypes.c_float, _P, _P, _P],
     "prim_div_mul": [_P, _P, _I64, _P, _P, _P],
-    "prim_pack16": [_I, _U32, _I64, _P, _P],
+    "prim_pack16": [_I, _U32, _I64, _P, _P, _P],
     "prim_upcast16": [_I, _P, _P],
-    "prim_sub_f16_pairs": [_I, _U32, _I64, _P, _P],
-    "prim_sub_f16": [_P, _P, _I64, _P, _P],
+    "prim_sub_f16_pairs": [_I, _U32, _I64, _P, _P, _P],
+    "prim_sub_f16": [_P, _P, _I64, _P, _P, _P],
 }
 
 
@@ -237,14 +237,17 @@ def test_multiplier_table_division_and_products(prim):
 
 @pytest.mark.parametrize("f16", [0, 1], ids=["bf16", "f16"])
 def test_output_rounding_every_binary32(prim, orc, f16):
-    """pack_bf16 / pack_f16 (the QDQ and dequantize outputs) round every
-    binary32 as the oracle does (RNE, overflow to inf, gradual underflow);
-    a NaN input gives a NaN."""
+    """pack_bf16 / pack_f16 (one packed convert: the QDQ and dequantize
+    outputs, and the binary16 rounding of the FP16-error mode) round every
+    binary32 as the oracle does (RNE, overflow to inf, gradual underflow),
+    in the low half and, swapped, in the high half; a NaN input gives a
+    NaN."""
     out = torch.empty(CHUNK // 2, dtype=torch.int32, device="cuda")
+    mismatch = torch.zeros(1, dtype=torch.int32, device="cuda")
     host = Host()
     conv = orc.f32_to_f16_bits if f16 else orc.f32_to_bf16_bits
     for base in range(0, 1 << 32, CHUNK):
-        assert prim.prim_pack16(f16, base, CHUNK // 2, _p(out), _s()) == 0
+        assert prim.prim_pack16(f16, base, CHUNK // 2, _p(out), _p(mismatch), _s()) == 0
         got = host.get(out).view(np.uint16)  # little-endian: element 2t, then 2t + 1
         x = _patterns(base, CHUNK)
         want = conv(x.view(np.float32))
@@ -252,6 +255,7 @@ def test_output_rounding_every_binary32(prim, orc, f16):
         assert np.all(_is_nan16(got[nan_in], f16)), "a NaN input did not give a NaN"
         _first_mismatch(np.where(nan_in, 0, got), np.where(nan_in, 0, want), x,
                         "f16 rounding" if f16 else "bf16 rounding")
+    assert int(mismatch.item()) == 0, "a value rounds differently in the low and the high half"
 
 
 @pytest.mark.parametrize("f16", [0, 1], ids=["bf16", "f16"])
@@ -273,15 +277,18 @@ def test_input_upcasts_every_16bit_pattern(prim, f16):
 
 @pytest.mark.parametrize("x_f16", [0, 1], ids=["bf16_x", "f16_x"])
 def test_fp16_error_difference_every_16bit_pair(prim, x_f16):
-    """sub_f16 (one v_fma_mix_f32: the binary16 operand times -1, plus x,
-    rounded once) equals IEEE RN(x - f32(h)) for every x of the 16-bit input
-    type and every binary16 h; NaN results agree as NaN."""
+    """sub_f16x2 (a packed binary16 convert, then per element one
+    v_fma_mix_f32: the binary16 operand times -1, plus x, rounded once)
+    equals IEEE RN(x - f32(h)) for every x of the 16-bit input type and
+    every binary16 h, in the low and in the high half; NaN results agree as
+    NaN."""
     out = torch.empty(CHUNK, dtype=torch.float32, device="cuda")
+    mismatch = torch.zeros(1, dtype=torch.int32, device="cuda")
     host = Host()
     h_val = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
     rows = CHUNK >> 16
     for base in range(0, 1 << 32, CHUNK):
-        assert prim.prim_sub_f16_pairs(x_f16, base, CHUNK, _p(out), _s()) == 0
+        assert prim.prim_sub_f16_pairs(x_f16, base, CHUNK, _p(out), _p(mismatch), _s()) == 0
         got = host.get(out).reshape(rows, 65536)
         xw = np.arange(base >> 16, (base >> 16) + rows, dtype=np.uint32)
         x = xw.astype(np.uint16).view(np.float16).astype(np.float32) if x_f16 else (xw << 16).view(np.float32)
@@ -292,12 +299,13 @@ def test_fp16_error_difference_every_16bit_pair(prim, x_f16):
         g = np.where(gn, 0, got).view(np.uint32).reshape(-1)
         w = np.where(wn, 0, want).view(np.uint32).reshape(-1)
         _first_mismatch(g, w, _patterns(base, CHUNK), "x - f32(h)")
+    assert int(mismatch.item()) == 0, "a difference depends on the half it is computed in"
 
 
 def test_fp16_error_difference_fp32_operands(prim, orc):
     """For fp32 inputs (x any binary32) and decoded values that are not
-    binary16 values, sub_f16(x, xh) = RN(x - f32(RN16(xh))) on a sample that
-    covers every binade, subnormals, overflow to inf and NaN."""
+    binary16 values, sub_f16x2 gives RN(x - f32(RN16(xh))) in either half, on
+    a sample that covers every binade, subnormals, overflow to inf and NaN."""
     rng = np.random.default_rng(11)
     n = 1 << 24
     x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
@@ -308,8 +316,10 @@ def test_fp16_error_difference_fp32_operands(prim, orc):
     xd = torch.from_numpy(x.view(np.float32)).to("cuda")
     hd = torch.from_numpy(xh.view(np.float32)).to("cuda")
     out = torch.empty_like(xd)
-    assert prim.prim_sub_f16(_p(xd), _p(hd), n, _p(out), _s()) == 0
+    mismatch = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert prim.prim_sub_f16(_p(xd), _p(hd), n, _p(out), _p(mismatch), _s()) == 0
     torch.cuda.synchronize()
+    assert int(mismatch.item()) == 0, "a difference depends on the half it is computed in"
     got = out.cpu().numpy()
     h = orc.f32_to_f16_bits(xh.view(np.float32)).view(np.float16).astype(np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
