@@ -487,6 +487,8 @@ def other_workloads(fos, synthdata, torch, np, stream, c5, steps=50, warmup=5):
         ms = float(np.median(time_loop(fn, ns, 200, 10)))
         out[key] = entry(nbytes, ms, **({"note": note} if note else {}))
         log(f"[bench] {key}: {out[key]['avg_launch_us']} us, {out[key]['GB/s']} GB/s")
+    out["fused_amax_quantize_bf16_8192x4096_phases"] = fused_phases(fos, torch, np, runs[
+        "fused_amax_quantize_bf16_8192x4096"][0], ns)
     del xs, codes, scales, ys, row_amax, ct, stt
 
     # 16x16 weights, bf16 4096x14336 and fp32 4096x4096, per-tensor, MSE exact, 448
@@ -568,6 +570,33 @@ PAGES_QDQ_MODES = (("nvfp4", "mse", 448), ("4over6", "mae", 448), ("4over6", "ma
                    ("4over6", "mse", 256))
 PAGES_QDQ_US = {"bf16": (156.813, 213.055, 213.064, 216.156, 216.315),
                 "fp16": (157.402, 213.018, 213.021, 213.625, 213.596)}
+
+
+def fused_phases(fos, torch, np, launch, n_sets):
+    """Per-wave phase times of one one-read fused launch (the library's
+    timestamp diagnostics) on a buffer set last read n_sets launches
+    earlier, after 20 untimed launches: microseconds after the earliest wave
+    start at which the waves' loads have landed, the barrier releases them
+    and they end."""
+    for i in range(20):
+        launch(i % n_sets)
+    buf = torch.zeros(65536, 4, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    khz = fos.set_phase_timestamps(buf)
+    try:
+        launch(20 % n_sets)
+        torch.cuda.synchronize()
+    finally:
+        fos.set_phase_timestamps(None)
+    t = buf.cpu().numpy()
+    t = t[t[:, 0] != 0]
+    us = (t - t[:, 0].min()) * (1e3 / khz)
+    pct = lambda c, qs: [round(float(np.percentile(us[:, c], q)), 2) for q in qs]
+    return {"waves": int(t.shape[0]), "clock_khz": khz,
+            "start_us_p50_max": pct(0, (50, 100)),
+            "loads_landed_us_min_p50_max": pct(1, (0, 50, 100)),
+            "barrier_released_us_min_max": pct(2, (0, 100)),
+            "end_us_min_p50_max": pct(3, (0, 50, 100))}
 
 
 # ---------------------------------------------------------------- profile pass

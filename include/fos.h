@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FOS_ABI_VERSION 5
+#define FOS_ABI_VERSION 6
 
 /* element types */
 #define FOS_BF16 0
@@ -152,6 +152,19 @@ const char* fos_last_error(void);
  * barrier completes when the rest of the grid arrives: the workspace is
  * left consistent and the next call on it is correct. */
 int fos_set_barrier_poll_limit(int polls);
+
+/* Diagnostics (added in ABI version 6). With d_buf non-NULL, every
+ * one-read fused launch (fos_quantize_fused or fos_qdq_fused on a tensor
+ * that fits on chip) enqueued from now on, process-wide, writes for each of
+ * its waves w < max_waves four values of the device's real-time counter to
+ * d_buf[4w .. 4w + 3]: the wave's start, the moment its phase-1 loads have
+ * landed, the moment the grid barrier releases it, and its end (a wave
+ * whose barrier gave up writes nothing). d_buf is a device buffer of
+ * 4 * max_waves uint64 values, owned by the caller and written by every
+ * such launch until this is called again with d_buf = NULL. *clock_khz
+ * (if non-NULL) receives the counter's rate in kHz. Calls whose launches
+ * overlap overwrite each other's values. */
+int fos_set_phase_timestamps(unsigned long long* d_buf, int64_t max_waves, int* clock_khz);
 
 /* Global amax: NaN-dropping max |x| with start value +0, per tensor
  * (out[1]), per row (out[M]) or per 16-row band (out[M], M % 16 == 0).

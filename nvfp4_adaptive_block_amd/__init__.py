@@ -59,6 +59,7 @@ _SIGS = {
     "fos_status_string": (ctypes.c_char_p, [_I]),
     "fos_last_error": (ctypes.c_char_p, []),
     "fos_set_barrier_poll_limit": (_I, [_I]),
+    "fos_set_phase_timestamps": (_I, [_P, _I64, _P]),
     "fos_amax": (_I, [_P, _I, _I64, _I64, _I, _P, _P]),
     "fos_quantize": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P, _P, _P, _P]),
     "fos_qdq": (_I, [_P, _I, _I64, _I64, _P, ctypes.POINTER(_Config), _P, _P]),
@@ -163,6 +164,23 @@ def set_barrier_poll_limit(polls: int) -> int:
     if prev < 0:
         raise ValueError(f"poll limit must be >= 0, got {polls}")
     return prev
+
+
+def set_phase_timestamps(buf: torch.Tensor | None) -> int:
+    """Diagnostics: the one-read fused kernels enqueued from now on write, per
+    wave, four real-time-counter values (start, loads landed, barrier
+    released, end) to buf (int64 [waves, 4] on the device); None stops it.
+    Returns the counter's rate in kHz."""
+    khz = ctypes.c_int(0)
+    if buf is None:
+        _check(load_library().fos_set_phase_timestamps(None, 0, ctypes.byref(khz)))
+    else:
+        if buf.dtype != torch.int64 or buf.dim() != 2 or buf.shape[1] != 4 or not buf.is_contiguous():
+            raise ValueError("buf must be a contiguous int64 [waves, 4] tensor")
+        with torch.cuda.device(buf.device):
+            _check(load_library().fos_set_phase_timestamps(ctypes.c_void_p(buf.data_ptr()), buf.shape[0],
+                                                           ctypes.byref(khz)))
+    return khz.value
 
 
 def _dev(device) -> torch.device:

@@ -20,6 +20,9 @@ thread_local std::string g_last_error;
 
 // Polls a fused call's grid barrier makes before giving up (process-wide).
 std::atomic<int> g_poll_limit{fos::kDefaultSpinLimit};
+// the one-read fused kernel's phase timestamps (diagnostics): buffer, waves
+std::atomic<unsigned long long*> g_phase_ts{nullptr};
+std::atomic<int64_t> g_phase_cap{0};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -190,6 +193,19 @@ const char* fos_last_error(void) { return g_last_error.c_str(); }
 int fos_set_barrier_poll_limit(int polls) {
   if (polls < 0) return -1;
   return g_poll_limit.exchange(polls, std::memory_order_relaxed);
+}
+
+int fos_set_phase_timestamps(unsigned long long* d_buf, int64_t max_waves, int* clock_khz) {
+  if (d_buf && (max_waves < 0 || !aligned(d_buf, 8))) return fail(FOS_ERR_INVALID_ARG, "bad timestamp buffer");
+  if (clock_khz) {
+    int dev = 0, khz = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) khz = 0;
+    *clock_khz = khz;
+  }
+  g_phase_cap.store(d_buf ? max_waves : 0, std::memory_order_relaxed);
+  g_phase_ts.store(d_buf, std::memory_order_relaxed);
+  return FOS_OK;
 }
 
 int fos_amax(const void* x, int dtype, int64_t M, int64_t K, int gran, float* amax_out, void* stream) {
@@ -487,6 +503,8 @@ int fos_quantize_fused(const void* x, int dtype, int64_t M, int64_t K, const fos
   a.sdec_out = sdec_out;
   a.status = d_status;
   a.spin_limit = g_poll_limit.load(std::memory_order_relaxed);
+  a.phase_ts = g_phase_ts.load(std::memory_order_relaxed);
+  a.phase_cap = g_phase_cap.load(std::memory_order_relaxed);
   if (cfg->scale_gran == FOS_PER_ROW) {  // per-row segments, one wave per row at a time
     a.total_units = M * ((a.t[0].K / 16 + ub - 1) / ub);
     return launch_status(fos::launch_fused_row(dtype, cfg->recipe, metric, prec, order, a, amax_out,
@@ -524,6 +542,8 @@ int fos_qdq_fused(const void* x, int dtype, int64_t M, int64_t K, const fos_conf
   a.six_b = six_b(cfg);
   a.status = d_status;
   a.spin_limit = g_poll_limit.load(std::memory_order_relaxed);
+  a.phase_ts = g_phase_ts.load(std::memory_order_relaxed);
+  a.phase_cap = g_phase_cap.load(std::memory_order_relaxed);
   bool done = false;
   if ((rc = launch_status(fos::launch_fused_qdq(dtype, cfg->recipe, metric, prec, order, a,
                                                 static_cast<uint32_t*>(workspace), amax_out, &done, s))))

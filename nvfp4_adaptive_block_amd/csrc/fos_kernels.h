@@ -76,6 +76,10 @@ struct Args1x16 {
   const int32_t* offs;       // grouped: cumulative end offsets [G]
   const float* group_amax;   // grouped: [G]
   int spin_limit;            // fused calls: polls before the grid barrier gives up
+  // nullable: the one-read fused kernel's per-wave phase timestamps (4 per
+  // wave, for waves below phase_cap)
+  unsigned long long* phase_ts;
+  int64_t phase_cap;
 };
 
 struct Args16x16 {

@@ -1640,6 +1640,21 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   const TensorRef& T = args.t[0];
   const int64_t nblk = T.M * (T.K >> 4);
   const Walk<DT, kGranTensor, OUT> W(T, args.codes, args.scales);
+  // diagnostics: the wave's real-time clock at its start, when its loads
+  // have landed, when the barrier releases it and at its end
+  const bool stamp = args.phase_ts != nullptr && wave < args.phase_cap;  // wave-uniform
+  uint64_t ts[3] = {0, 0, 0};
+  if (stamp) ts[0] = __builtin_amdgcn_s_memrealtime();
+  auto finish = [&]() {
+    if (stamp && lane == 0) {
+      const uint64_t t3 = __builtin_amdgcn_s_memrealtime();
+      unsigned long long* o = args.phase_ts + 4 * wave;
+      o[0] = ts[0];
+      o[1] = ts[1];
+      o[2] = ts[2];
+      o[3] = t3;
+    }
+  };
 
   // phase 1: read every unit once; units past the wave's range have empty
   // resources (their loads read zeros and are never used)
@@ -1657,6 +1672,7 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
     for (int j = 0; j < kNB; j++) R[r][j].load(U.x, unit_block_of_lane<DT, OUT>(lane) * kB + j * 64 * kB);
   }
   vm_wait();  // the loads, the LDS-bound ones included, have landed
+  if (stamp) ts[1] = __builtin_amdgcn_s_memrealtime();
   PieceMax<DT> pm;
 #pragma unroll
   for (int t = 0; t < kOnchipLds; t++) {
@@ -1687,6 +1703,7 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   }
   __syncthreads();
   if (!ok) return;
+  if (stamp) ts[2] = __builtin_amdgcn_s_memrealtime();
   const float A = __uint_as_float(amax_bits);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (amax_out) amax_out[0] = A;
@@ -1694,7 +1711,10 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
   }
 
   // phase 2: the register units, then the staged ones
-  if (u >= u_end) return;
+  if (u >= u_end) {
+    finish();
+    return;
+  }
   const float S_enc = global_encode_scale(A, args.six_b);
   const float S_dec = 1.0f / S_enc;
   tab.build(S_enc, S_dec, lane);
@@ -1714,6 +1734,7 @@ __global__ void __launch_bounds__(256) k_fused_onchip(const Args1x16<1> args, ui
       unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, OUT>(q, S_enc, S_dec, tab, W.unit(W.at(v), true, T.M), lane);
     }
   }
+  finish();
 }
 
 // ------------------------------------------------------------ fused per-row amax + quantize

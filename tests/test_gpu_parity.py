@@ -726,6 +726,39 @@ def test_qdq_fused(orc, dtype):
     assert int(status.item()) == 0
 
 
+def test_fused_phase_timestamps(orc):
+    """Diagnostics of the one-read fused quantize: with a timestamp buffer
+    set, every wave writes its start, loads-landed, barrier-release and end
+    times in that order, rows past the grid stay untouched, and the outputs
+    still match the oracle."""
+    M, K = 2048, 4096
+    x = synthdata.normal(M, K, 91, "bf16")
+    b = raw_bits(x)
+    buf = torch.zeros(16384, 4, dtype=torch.int64, device="cuda")
+    khz = fos.set_phase_timestamps(buf)
+    try:
+        codes, scales, amax, _ = fos.fos_quantize_fused(dev(x), check=True, recipe="4over6")
+        torch.cuda.synchronize()
+    finally:
+        fos.set_phase_timestamps(None)
+    assert khz > 0
+    t = buf.cpu().numpy()
+    used = t[:, 0] != 0
+    n = int(used.sum())
+    assert n > 0 and used[:n].all() and not used[n:].any(), "waves 0 .. n-1 write, no other row"
+    assert (np.diff(t[:n], axis=1) >= 0).all(), "phases out of order"
+    a = orc.amax(b, "bf16", "tensor")
+    want = orc.quantize(b, "bf16", a, recipe="4over6")
+    np.testing.assert_array_equal(amax.cpu().numpy().view(np.uint32), a.view(np.uint32))
+    np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+    np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+    # off again: a later launch writes nothing
+    buf.zero_()
+    fos.fos_quantize_fused(dev(x), check=True, recipe="4over6")
+    torch.cuda.synchronize()
+    assert not buf.any()
+
+
 def test_qdq_fused_stage_lanes_past_the_end(orc):
     """As for the fused quantize: stage lanes past a ragged tensor's end hold
     an earlier launch's values, which must not count in the amax."""

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_host_only_calls():
     lib = fos.load_library()
-    assert lib.fos_abi_version() == 5
+    assert lib.fos_abi_version() == 6
     assert lib.fos_status_string(0) == b"ok"
     assert lib.fos_status_string(3) == b"unsupported shape"
     # a shape error is reported before any device is touched
