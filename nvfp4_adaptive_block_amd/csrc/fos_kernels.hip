@@ -14,9 +14,12 @@
 // Work mapping, 1x16 blocks: one lane owns one 16-element block, so the
 // block amax, both candidates, the 16-term error tree and the selection stay
 // in that lane's registers. A wave covers a unit of 64 consecutive blocks
-// (2 KiB of bf16 read with 128-bit loads) and walks a contiguous range of
-// units, loading the next unit while it computes the current one. The grid
-// holds only as many workgroups as are resident at once.
+// (2 KiB of bf16 read with 128-bit loads) and walks its units two at a time,
+// loading the next unit while it computes the current one. A single
+// tensor's units go out in pairs dealt round robin over the waves (the waves
+// in flight share one window moving through the tensor); list and per-row
+// launches give each wave a contiguous range. The grid holds only as many
+// workgroups as are resident at once.
 //
 // Per-block division is replaced by a table: the block scale sigma is one of
 // 127 E4M3 values, so for each global scale the wave keeps, in LDS, the
@@ -492,6 +495,26 @@ struct Walk {
     }
     return p;
   }
+  // Moving a position n units ahead: the row and segment steps of n units,
+  // taken once, then one carry per move (segments stay below their limit).
+  struct Step {
+    int64_t n, drow, dseg;
+  };
+  __device__ Step step_of(int64_t n) const {
+    if (GRAN == kGranTensor) return Step{n, 0, 0};
+    const int64_t b = flat ? n * kUnitBlocks : n, lim = flat ? nbk : spr;
+    return Step{n, b / lim, b - (b / lim) * lim};
+  }
+  __device__ UPos advance(UPos p, const Step& st) const {
+    p.v += st.n;
+    if (GRAN != kGranTensor) {
+      const int64_t lim = flat ? nbk : spr;
+      p.row += st.drow;
+      p.seg += st.dseg;
+      if (p.seg >= lim) { p.seg -= lim; p.row += 1; }
+    }
+    return p;
+  }
   // resources for the unit at p (valid: the unit exists; rows_read: rows of
   // the tensor that hold data, later rows read as zeros)
   __device__ Unit unit(const UPos& p, bool valid, int64_t rows_read) const {
@@ -580,13 +603,16 @@ __device__ __forceinline__ void zero_unit_1x16(const Unit& U, int lane) {
   }
 }
 
-// The unit range [u, u_end) of one wave of a 1x16 launch. With FUSED the
-// amaxes come from `fused_amax` (LDS, as float bits) rather than from
-// memory: per-tensor scales [n], one per tensor of the launch; grouped
-// scales [G]; per-row scales [1], the amax of the one row the range covers.
+// The units of one wave of a 1x16 launch: pairs u, u + 1, then u + stride,
+// u + stride + 1, and so on, below u_end. stride 2 walks a contiguous range
+// [u, u_end) (over the tensors of a list); a larger stride deals pairs out
+// round robin over a single tensor's units. With FUSED the amaxes come from
+// `fused_amax` (LDS, as float bits) rather than from memory: per-tensor
+// scales [n], one per tensor of the launch; grouped scales [G]; per-row
+// scales [1], the amax of the one row the range covers.
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT, bool FUSED>
 __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table& tab, int lane, int64_t u,
-                                          int64_t u_end, const uint32_t* fused_amax) {
+                                          int64_t u_end, const uint32_t* fused_amax, int64_t stride = 2) {
   constexpr int kB = Raw<DT>::kBytes;
   constexpr int kNB = unit_blocks(OUT, DT) / 64;
   const int64_t total = args.total_units;
@@ -615,6 +641,15 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
     int64_t tab_amax = -1;  // amax bits of the current table; -1: none built yet
     int64_t g_lo = 0, g_hi = 0;
     int g_cur = -1;
+    // up to 64 groups: lane g holds offs[g] (and the group's amax bits), so
+    // a row's group is a count of lanes rather than a chain of loads
+    const bool lane_groups = GRAN == kGranGroup && args.G <= 64;
+    int32_t offs_l = INT32_MAX;
+    uint32_t gam_l = 0;
+    if (GRAN == kGranGroup && lane_groups && lane < args.G) {
+      offs_l = args.offs[lane];
+      if (!FUSED) gam_l = __float_as_uint(args.group_amax[lane]);
+    }
 
     // one unit: quantize the lane's block held in `raw`, store its outputs
     // (two stores). Units past the range compute on zeros and their stores
@@ -635,12 +670,18 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
           if (GRAN == kGranRow) {
             A = FUSED ? __uint_as_float(fused_amax[0]) : ld_const(T.amax, row);
           } else {
-            if (row < g_lo || row >= g_hi) {
+            if (lane_groups) {
+              // the groups that end at or before the row precede it (a data
+              // row lies below offs[G-1] <= INT32_MAX)
+              g_cur = min((int)__builtin_popcountll(__ballot(offs_l <= (int32_t)row)), args.G - 1);
+            } else if (row < g_lo || row >= g_hi) {
               g_cur = group_of(args.offs, args.G, row);
               g_lo = g_cur ? (int64_t)ld_const(args.offs, g_cur - 1) : 0;
               g_hi = (g_cur == args.G - 1) ? INT64_MAX : (int64_t)ld_const(args.offs, g_cur);
             }
-            A = FUSED ? __uint_as_float(fused_amax[g_cur]) : ld_const(args.group_amax, g_cur);
+            A = FUSED ? __uint_as_float(fused_amax[g_cur])
+                      : lane_groups ? __uint_as_float(__builtin_amdgcn_readlane(gam_l, g_cur))
+                                    : ld_const(args.group_amax, g_cur);
           }
           if ((int64_t)__float_as_uint(A) != tab_amax) {
             S_enc = global_encode_scale(A, six_b);
@@ -665,6 +706,7 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
     // unit before the first), and the compiler's wait counts only the loads
     // issued since.
     const int64_t v_stop = stop - T.unit_begin;
+    const auto st = W.step_of(stride);
     UPos pa = W.at(u - T.unit_begin);
     UPos pb = W.next(pa);
     Unit UA = W.unit(pa, true, rows_read);
@@ -675,11 +717,11 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
     load_unit(B, UB);
     for (; pa.v < v_stop;) {
       process(A, pa, true, UA);
-      pa = W.next(pb);
+      pa = W.advance(pa, st);
       UA = W.unit(pa, pa.v < v_stop, rows_read);
       load_unit(A, UA);
       process(B, pb, pb.v < v_stop, UB);
-      pb = W.next(pa);
+      pb = W.advance(pb, st);
       UB = W.unit(pb, pb.v < v_stop, rows_read);
       load_unit(B, UB);
     }
@@ -729,18 +771,34 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
 
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
+  // A single tensor's units go out in pairs dealt round robin, so that the
+  // waves in flight work inside one window that moves through the tensor;
+  // the tensors of a list, and per-row units (a table per row), go out as
+  // contiguous ranges.
+  const bool rr = args.n == 1 && GRAN != kGranRow;
+  const int64_t stride = rr ? 2 * nwaves : 2;
   int64_t u, u_end;
+  auto share = [&](int64_t begin, int64_t end) {
+    if (rr) {
+      u = begin + 2 * wave;
+      u_end = end;
+    } else {
+      wave_range(begin, end, wave, nwaves, u, u_end);
+    }
+  };
   if (GRAN == kGranGroup) {
     // the data units, then the padding units (zero outputs, nothing
     // computed), each dealt out evenly, so that no wave holds only padding
     const int64_t D = grouped_data_units<DT>(args);
-    wave_range(0, D, wave, nwaves, u, u_end);
-    if (u < u_end) walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr);
-    wave_range(D, args.total_units, wave, nwaves, u, u_end);
+    share(0, D);
+    if (u < u_end)
+      walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr, stride);
+    share(D, args.total_units);
   } else {
-    wave_range(0, args.total_units, wave, nwaves, u, u_end);
+    share(0, args.total_units);
   }
-  if (u < u_end) walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr);
+  if (u < u_end)
+    walk_1x16<NT, DT, RECIPE, METRIC, PREC, ORDER, GRAN, OUT, false>(args, tab, lane, u, u_end, nullptr, stride);
 }
 
 // NaN-dropping magnitude max over packed 16-bit pairs: with m = |h| bits,
@@ -1869,8 +1927,9 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
   const int G = args.G;
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  // the data units, then the padding units, each dealt out evenly (phase 1
-  // reads only data rows; phase 2 writes zeros for the padding units)
+  // phase 1 reads the data rows, each wave a contiguous range of the data
+  // units; phase 2 takes the data units, then the padding units (zeros
+  // written), in pairs dealt round robin as in the grouped quantize
   const int64_t D = grouped_data_units<DT>(args);
   int64_t u, u_end;
   wave_range(0, D, wave, nwaves, u, u_end);
@@ -1946,10 +2005,14 @@ __global__ void __launch_bounds__(256) k_fused_grouped(const Args1x16<1> args, u
     }
   }
 
-  // phase 2
-  if (u < u_end) walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, u_end, gm);
-  wave_range(D, args.total_units, wave, nwaves, u, u_end);
-  if (u < u_end) walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, u_end, gm);
+  // phase 2 (the pairs dealt round robin: no better for phase 1's reads)
+  const int64_t stride = 2 * nwaves;
+  u = 2 * wave;
+  if (u < D) walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, D, gm, stride);
+  u = D + 2 * wave;
+  if (u < args.total_units)
+    walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranGroup, kOutQuant, true>(args, tab, lane, u, args.total_units, gm,
+                                                                               stride);
 }
 
 // ------------------------------------------------------------ fused amaxes + QDQ list
@@ -2043,7 +2106,7 @@ static unsigned small_grid(int64_t n) {
 }
 
 // Workgroups of 256 threads resident at once for kernel fn: the grid of the
-// unit-walking kernels (each wave then walks a contiguous unit range).
+// unit-walking kernels (each wave then walks its share of the units).
 static int64_t num_cus() {
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
