@@ -237,19 +237,21 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* p, int64_t i) {
 // Per-wave LDS table of the multipliers of all E4M3 codes for one global
 // scale: E[c] = RN(S_enc / sigma_c) (0 for sigma = 0, FLT_MAX on overflow),
 // D[c] = RN(sigma_c * S_dec). Codes never exceed 0x7E (scales saturate).
+// One code's entries (c < 128; code 0x7F, the E4M3 NaN, gets zeros).
+__device__ __forceinline__ void table_entry(int c, float S_enc, float S_dec, float* E, float* D) {
+  const float sigma = e4m3_value((uint32_t)c);
+  const bool zero = sigma == 0.0f || c >= 0x7F;
+  const float e = S_enc / (zero ? 1.0f : sigma);
+  E[c] = zero ? 0.0f : __builtin_fminf(e, kFltMax);
+  D[c] = (c >= 0x7F) ? 0.0f : sigma * S_dec;
+}
+
 struct Table {
   float* E;
   float* D;
   __device__ void build(float S_enc, float S_dec, int lane) const {
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int c = lane + 64 * k;
-      const float sigma = e4m3_value((uint32_t)c);
-      const bool zero = sigma == 0.0f || c >= 0x7F;
-      const float e = S_enc / (zero ? 1.0f : sigma);
-      E[c] = zero ? 0.0f : __builtin_fminf(e, kFltMax);
-      D[c] = (c >= 0x7F) ? 0.0f : sigma * S_dec;
-    }
+    for (int k = 0; k < 2; k++) table_entry(lane + 64 * k, S_enc, S_dec, E, D);
     // the lanes of this wave read what other lanes wrote
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -731,6 +733,71 @@ __device__ __forceinline__ void walk_1x16(const Args1x16<NT>& args, const Table&
   }
 }
 
+// Lists of up to kListTables tensors with per-tensor scales: every tensor's
+// table is built once per workgroup, in LDS, so that the units of the whole
+// list can go out in pairs dealt round robin over the waves (the waves in
+// flight then share one window moving through the list) without a table
+// rebuilt per pair. tabs[i] holds tensor i's E (first 128) and D entries,
+// scl[i] its S_enc and S_dec.
+constexpr int kListTables = 16;
+
+template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int OUT>
+__device__ __forceinline__ void walk_list_rr(const Args1x16<NT>& args, float (*tabs)[256], const float (*scl)[2],
+                                             int lane, int64_t u, int64_t stride) {
+  static_assert(OUT == kOutQdq, "lists are quantize-dequantize launches");
+  constexpr int kB = Raw<DT>::kBytes;
+  constexpr int kNB = unit_blocks(OUT, DT) / 64;
+  constexpr int64_t kUB = unit_blocks(OUT, DT);
+  const int64_t total = args.total_units;
+  const uint32_t off_x = unit_block_of_lane<DT, OUT>(lane) * kB;
+  struct LPos {
+    int64_t g;  // unit of the launch
+    int ti;     // its tensor (the last one past the end)
+  };
+  auto locate = [&](int64_t g, int ti) {  // units only move forward
+    while (ti + 1 < args.n && args.t[ti + 1].unit_begin <= g) ti++;
+    return LPos{g, ti};
+  };
+  auto unit = [&](const LPos& p) {
+    const TensorRef& T = args.t[p.ti];
+    const int64_t b0 = (p.g - T.unit_begin) * kUB;
+    const int64_t nvalid = p.g < total ? min(kUB, T.M * (T.K >> 4) - b0) : 0;
+    Unit U;
+    U.x = make_rsrc(static_cast<const char*>(T.x) + b0 * kB, nvalid * kB);
+    U.out = make_rsrc(static_cast<char*>(T.y) + b0 * kB, nvalid * kB);
+    U.scl = U.out;
+    return U;
+  };
+  auto load_unit = [&](Raw<DT>* r, const Unit& U) {
+#pragma unroll
+    for (int j = 0; j < kNB; j++) r[j].load(U.x, off_x + j * 64 * kB);
+  };
+  // a unit past the end computes on zeros; its stores fall outside its
+  // resources
+  auto process = [&](const Raw<DT>* raw, const LPos& p, const Unit& U) {
+    const Table tab{tabs[p.ti], tabs[p.ti] + 128};
+    unit_1x16<DT, RECIPE, METRIC, PREC, ORDER, OUT>(raw, scl[p.ti][0], scl[p.ti][1], tab, U, lane);
+  };
+  // two units in flight, as in walk_1x16
+  LPos pa = locate(u, 0);
+  LPos pb = locate(u + 1, pa.ti);
+  Unit UA = unit(pa), UB = unit(pb);
+  Raw<DT> A[kNB], B[kNB];
+  load_unit(A, UA);
+  dummy_stores<kNB>();
+  load_unit(B, UB);
+  while (pa.g < total) {
+    process(A, pa, UA);
+    pa = locate(pa.g + stride, pa.ti);
+    UA = unit(pa);
+    load_unit(A, UA);
+    process(B, pb, UB);
+    pb = locate(pb.g + stride, pb.ti);
+    UB = unit(pb);
+    load_unit(B, UB);
+  }
+}
+
 // The wave's share [u, u_end) of units [begin, end): contiguous ranges in
 // wave order, of n / nwaves units and one more for the first n % nwaves
 // waves. Waves are numbered round by round (workgroup b holds waves 4b ..
@@ -762,7 +829,9 @@ __device__ __forceinline__ int64_t grouped_data_units(const Args1x16<NT>& args) 
 
 template <int NT, int DT, int RECIPE, int METRIC, int PREC, int ORDER, int GRAN, int OUT>
 __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
-  __shared__ float lds[4][256];
+  constexpr bool kList = NT > 1 && OUT == kOutQdq && GRAN == kGranTensor;
+  __shared__ float lds[kList ? kListTables : 4][256];  // a table per wave, or per tensor of a list
+  __shared__ float lscl[kList ? kListTables : 1][2];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const Table tab{lds[wv], lds[wv] + 128};
@@ -771,6 +840,24 @@ __global__ void __launch_bounds__(256) k_1x16(const Args1x16<NT> args) {
 
   const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
+  if constexpr (kList) {
+    if (args.n > 1 && args.n <= kListTables) {
+      // every tensor's scales, then its table, shared by the workgroup
+      if (threadIdx.x < args.n) {
+        const float S_enc = global_encode_scale(ld_const(args.t[threadIdx.x].amax, 0), args.six_b);
+        lscl[threadIdx.x][0] = S_enc;
+        lscl[threadIdx.x][1] = 1.0f / S_enc;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < args.n * 128; i += blockDim.x)
+        table_entry(i & 127, lscl[i >> 7][0], lscl[i >> 7][1], lds[i >> 7], lds[i >> 7] + 128);
+      __syncthreads();
+      const int64_t u = 2 * wave;
+      if (u < args.total_units)
+        walk_list_rr<NT, DT, RECIPE, METRIC, PREC, ORDER, OUT>(args, lds, lscl, lane, u, 2 * nwaves);
+      return;
+    }
+  }
   // A single tensor's units go out in pairs dealt round robin, so that the
   // waves in flight work inside one window that moves through the tensor;
   // the tensors of a list, and per-row units (a table per row), go out as
@@ -966,8 +1053,12 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   const int64_t K = args.K, nbk = K >> 4;
   const int64_t gpb = (nbk + kT - 1) / kT;  // units per band
   const int64_t total = (args.M >> 4) * gpb;
-  int64_t u, u_end;
-  wave_range(0, total, wave, nwaves, u, u_end);
+  // per-tensor scales: units dealt round robin over the waves (the waves in
+  // flight share one window of the tensor); per-row scales (a table per
+  // band): contiguous ranges
+  const int64_t stride = GRAN == kGranTensor ? nwaves : 1;
+  int64_t u = wave, u_end = total;
+  if (GRAN != kGranTensor) wave_range(0, total, wave, nwaves, u, u_end);
   const float six_b = args.six_b;
 
   if (OUT == kOutQuant && args.sdec_out) {
@@ -1005,8 +1096,11 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   struct P16 {
     int64_t band, tg;
   };
+  const int64_t sb = stride / gpb, st = stride - sb * gpb;  // bands and unit groups per step
   auto advance = [&](P16 p) {
-    if (++p.tg == gpb) { p.tg = 0; ++p.band; }
+    p.tg += st;
+    p.band += sb;
+    if (p.tg >= gpb) { p.tg -= gpb; ++p.band; }
     return p;
   };
   auto unit = [&](const P16& p, bool valid) {
@@ -1037,9 +1131,9 @@ __global__ void __launch_bounds__(256) k_16x16(const Args16x16 args) {
   U16 U = unit(p, true);
   Raw<DT> raw[kRPL];
   load(raw, U);
-  for (; u < u_end; u++) {
+  for (; u < u_end; u += stride) {
     const P16 pn = advance(p);
-    const U16 Un = unit(pn, u + 1 < u_end);
+    const U16 Un = unit(pn, u + stride < u_end);
     if (GRAN == kGranRow && p.band != cur_band) {
       // tile-uniform contract: the band uses its first row's amax, and a band
       // whose rows differ is flagged
@@ -2033,7 +2127,8 @@ __global__ void __launch_bounds__(256) k_fused_list(const Args1x16<kMaxList> arg
   constexpr int kA = __HIP_MEMORY_SCOPE_AGENT;
   constexpr int kR = __ATOMIC_RELAXED;
   constexpr int kUB = unit_blocks(kOutQdq, DT);
-  __shared__ float lds[4][256];
+  __shared__ float lds[kListTables][256];  // a table per wave, or per tensor (phase 2 of short lists)
+  __shared__ float lscl[kListTables][2];
   __shared__ uint32_t gm[kMaxList];
   __shared__ uint32_t gen0, bank;
   __shared__ int ok;
@@ -2092,7 +2187,23 @@ __global__ void __launch_bounds__(256) k_fused_list(const Args1x16<kMaxList> arg
     for (int t = threadIdx.x; t < n; t += blockDim.x)
       if (args.t[t].amax_out) args.t[t].amax_out[0] = __uint_as_float(gm[t]);
 
-  // phase 2
+  // phase 2: up to kListTables tensors, the units of the list in pairs dealt
+  // round robin with every tensor's table in LDS, as the QDQ list takes them;
+  // longer lists, the wave's contiguous range
+  if (n <= kListTables) {
+    if (threadIdx.x < n) {
+      const float S_enc = global_encode_scale(__uint_as_float(gm[threadIdx.x]), args.six_b);
+      lscl[threadIdx.x][0] = S_enc;
+      lscl[threadIdx.x][1] = 1.0f / S_enc;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n * 128; i += blockDim.x)
+      table_entry(i & 127, lscl[i >> 7][0], lscl[i >> 7][1], lds[i >> 7], lds[i >> 7] + 128);
+    __syncthreads();
+    if (2 * wave < args.total_units)
+      walk_list_rr<kMaxList, DT, RECIPE, METRIC, PREC, ORDER, kOutQdq>(args, lds, lscl, lane, 2 * wave, 2 * nwaves);
+    return;
+  }
   if (u >= u_end) return;
   walk_1x16<kMaxList, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQdq, true>(args, tab, lane, u, u_end, gm);
 }

@@ -276,6 +276,28 @@ def test_qdq_single_and_many_tensors(orc):
     np.testing.assert_array_equal(bits_of(y0), bits_of(ys[0]))
 
 
+@pytest.mark.parametrize("n", [2, 16, 17])
+def test_qdq_list_table_limit(orc, n):
+    """Lists of up to 16 tensors take the launch's units round robin with a
+    table per tensor in LDS; 17 take contiguous ranges. Both sides of the
+    limit, with ragged shapes, an empty tensor and tensors smaller than a
+    unit, for the plain and the fused-amax list."""
+    shapes = [(16 + 16 * (i % 4), 16 * (1 + (7 * i) % 23)) for i in range(n)]
+    shapes[n // 2] = (0, 48)
+    ws = [synthdata.weight(max(M, 1), K, 500 + i, "fp16")[:M].contiguous() for i, (M, K) in enumerate(shapes)]
+    amaxes = [orc.amax(raw_bits(w), "fp16", "tensor") if w.numel() else np.zeros(1, np.float32) for w in ws]
+    kw = dict(recipe="4over6", err_metric="mae", err_prec="exact", bound=256)
+    ys = fos.fos_qdq_list([dev(w) for w in ws], [dev(torch.from_numpy(a)) for a in amaxes], **kw)
+    ysf, amf = fos.fos_qdq_list_fused([dev(w) for w in ws], **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(amf.cpu().numpy().view(np.uint32), np.concatenate(amaxes).view(np.uint32))
+    for i, (w, a) in enumerate(zip(ws, amaxes)):
+        if w.numel():
+            want = orc.qdq(raw_bits(w), "fp16", a, **kw)
+            np.testing.assert_array_equal(bits_of(ys[i]), want, err_msg=f"tensor {i} of {n}")
+            np.testing.assert_array_equal(bits_of(ysf[i]), want, err_msg=f"fused: tensor {i} of {n}")
+
+
 def _fused_list_inputs(dtype):
     """A list with ragged widths, a one-block tensor, an empty tensor, an
     all-zero tensor, one with NaN and infinities, and one spanning several
