@@ -1697,9 +1697,10 @@ __global__ void __launch_bounds__(256) k_fused(const Args1x16<1> args, uint32_t*
     if (args.sdec_out) args.sdec_out[0] = 1.0f / global_encode_scale(A, args.six_b);
   }
 
-  // phase 2
-  if (u >= u_end) return;
-  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQuant, true>(args, tab, lane, u, u_end, &amax_bits);
+  // phase 2: pairs of units dealt round robin, as the quantize takes them
+  if (2 * wave >= args.total_units) return;
+  walk_1x16<1, DT, RECIPE, METRIC, PREC, ORDER, kGranTensor, kOutQuant, true>(args, tab, lane, 2 * wave,
+                                                                              args.total_units, &amax_bits, 2 * nwaves);
 }
 
 // ------------------------------------------------------------ on-chip fused amax + quantize
