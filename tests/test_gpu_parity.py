@@ -437,6 +437,34 @@ def test_grouped_flat_units(orc, dtype, K):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("G", [64, 65, 130])
+@pytest.mark.parametrize("K", [128, 272])
+def test_grouped_many_groups(orc, G, K):
+    """Up to 64 groups are looked up from offsets held one per lane; more go
+    through the binary search over offs. Both sides of that limit, with flat
+    (K = 128) and per-row (K = 272) units, many empty groups, the plain and
+    the fused grouped quantize."""
+    M, pad = 1536, 32
+    x, offs, _ = synthdata.grouped_tokens(M, pad, K, G, seeds=(91, 92, 93, 94), dtype="bf16")
+    b = raw_bits(x)
+    gam = _group_amaxes(orc, b, "bf16", offs)
+    kw = dict(recipe="4over6", err_metric="mse", err_prec="exact")
+    want = orc.quantize_grouped(b, "bf16", offs, gam, **kw)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(fos.FUSED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    codes, scales, _ = fos.fos_quantize_grouped(dev(x), dev(torch.from_numpy(offs)), dev(torch.from_numpy(gam)),
+                                                status=status, **kw)
+    fc, fs, am, _ = fos.fos_quantize_grouped_fused(dev(x), dev(torch.from_numpy(offs)), workspace=ws, status=status,
+                                                   **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes.cpu().numpy(), want["codes"])
+    np.testing.assert_array_equal(scales.cpu().numpy(), want["scales"])
+    np.testing.assert_array_equal(am.cpu().numpy().view(np.uint32), gam.view(np.uint32))
+    np.testing.assert_array_equal(fc.cpu().numpy(), want["codes"])
+    np.testing.assert_array_equal(fs.cpu().numpy(), want["scales"])
+    assert int(status.item()) == 0
+
+
 def test_grouped_empty_groups_and_bad_offsets(orc):
     K = 64
     x = synthdata.normal(96, K, 3, "bf16")
