@@ -2218,8 +2218,7 @@ static unsigned small_grid(int64_t n) {
   return (unsigned)(g < 1 ? 1 : (g > 1024 ? 1024 : g));
 }
 
-// Workgroups of 256 threads resident at once for kernel fn: the grid of the
-// unit-walking kernels (each wave then walks its share of the units).
+// compute units of the current device
 static int64_t num_cus() {
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
@@ -2227,6 +2226,8 @@ static int64_t num_cus() {
   return cus;
 }
 
+// Workgroups of 256 threads resident at once for kernel fn: the grid of the
+// unit-walking kernels (each wave then walks its share of the units).
 static int64_t resident_grid(const void* fn) {
   int dev = 0, cus = 0, per_cu = 0;
   (void)hipGetDevice(&dev);
